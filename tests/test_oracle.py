@@ -1,0 +1,285 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants, a library
+routine, and planted mistakes that the pins must catch.
+
+Nothing here touches a GPU or the HIP library.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.attention as OA
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("S", [1, 2, 3, 8, 17, 32])
+@pytest.mark.parametrize("D", [1, 4, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_matches_bruteforce(S, D, causal):
+    q, k, v = (_rand((S, D), s) for s in (11 * S + D, 12 * S + D, 13 * S + D))
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle.attention_fwd(q, k, v, causal, scale)
+    ob, lb = oracle.attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), causal, scale)
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lb), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- closed forms
+
+def _eval(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"e": math.e, "ln": math.log}))
+
+
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_closed_forms(case, causal):
+    q, k, v = (np.array(case[n], dtype=np.float64) for n in ("q", "k", "v"))
+    exp = case["causal" if causal else "noncausal"]
+    o, lse = oracle.attention_fwd(q, k, v, causal, case["scale"])
+    np.testing.assert_allclose(o, [[_eval(x) for x in r] for r in exp["o"]], atol=1e-14)
+    np.testing.assert_allclose(lse, [_eval(x) for x in exp["lse"]], atol=1e-14)
+
+
+# --------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one(causal):
+    q, k = _rand((40, 16), 1), _rand((40, 16), 2)
+    p = oracle.attention_probs(q, k, causal, 0.25)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    if causal:
+        assert np.all(np.triu(p, 1) == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_returns_constant(causal):
+    q, k = _rand((33, 8), 3, std=3.0), _rand((33, 8), 4, std=3.0)
+    v = np.full((33, 8), 0.7311)
+    o, _ = oracle.attention_fwd(q, k, v, causal, 0.5)
+    np.testing.assert_allclose(o, 0.7311, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mag", [1.0, 400.0])
+def test_identical_keys_mean_and_lse(causal, mag):
+    """All keys equal: every visible key has the same weight.
+
+    O_i is the mean of the visible V rows and lse_i = scale*q_i.k + ln(n_i).
+    mag=400 makes the logits ~1e3 so that a missing max-subtraction overflows.
+    """
+    S, D = 24, 6
+    q = _rand((S, D), 5) * mag
+    kk = _rand((1, D), 6)
+    k = np.repeat(kk, S, axis=0)
+    v = _rand((S, D), 7)
+    scale = 0.75
+    o, lse = oracle.attention_fwd(q, k, v, causal, scale)
+    n = np.arange(1, S + 1) if causal else np.full(S, S)
+    mean = np.cumsum(v, axis=0) / n[:, None] if causal else np.repeat(v.mean(0, keepdims=True), S, 0)
+    np.testing.assert_allclose(o, mean, atol=1e-11)
+    np.testing.assert_allclose(lse, scale * (q @ kk[0]) + np.log(n), rtol=1e-13, atol=1e-9)
+
+
+def test_causal_row0_is_v0():
+    q, k, v = _rand((16, 8), 8), _rand((16, 8), 9), _rand((16, 8), 10)
+    o, lse = oracle.attention_fwd(q, k, v, True, 0.3)
+    np.testing.assert_array_equal(o[0], v[0])
+    assert abs(lse[0] - 0.3 * float(q[0] @ k[0])) < 1e-14
+
+
+def test_causal_rows_ignore_future_keys():
+    S, D = 20, 8
+    q, k, v = _rand((S, D), 11), _rand((S, D), 12), _rand((S, D), 13)
+    o, lse = oracle.attention_fwd(q, k, v, True, 0.4)
+    for i in (0, 5, 13):
+        k2, v2 = k.copy(), v.copy()
+        k2[i + 1:] = _rand((S - i - 1, D), 100 + i) * 50
+        v2[i + 1:] = _rand((S - i - 1, D), 200 + i) * 50
+        o2, lse2 = oracle.attention_fwd(q, k2, v2, True, 0.4)
+        np.testing.assert_array_equal(o2[: i + 1], o[: i + 1])
+        np.testing.assert_array_equal(lse2[: i + 1], lse[: i + 1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_logit_shift(causal):
+    """K += w shifts row i's logits by scale*q_i.w: O unchanged, lse moves by it."""
+    S, D = 30, 8
+    q, k, v = _rand((S, D), 14), _rand((S, D), 15), _rand((S, D), 16)
+    w = _rand((D,), 17)
+    scale = 0.35
+    o, lse = oracle.attention_fwd(q, k, v, causal, scale)
+    o2, lse2 = oracle.attention_fwd(q, k + w, v, causal, scale)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2 - lse, scale * (q @ w), atol=1e-12)
+
+
+def test_attention_rows_equals_full():
+    S, D = 50, 16
+    q, k, v = _rand((S, D), 18), _rand((S, D), 19), _rand((S, D), 20)
+    o, lse = oracle.attention_fwd(q, k, v, True, 0.25)
+    rows = np.array([0, 7, 31, 49])
+    orr, lr = oracle.attention_rows(q, k, v, rows, True, 0.25)
+    np.testing.assert_allclose(orr, o[rows], atol=1e-14)
+    np.testing.assert_allclose(lr, lse[rows], atol=1e-14)
+
+
+def test_batched_shapes():
+    q = _rand((2, 3, 10, 4), 21)
+    k = _rand((2, 3, 10, 4), 22)
+    v = _rand((2, 3, 10, 4), 23)
+    o, lse = oracle.attention_fwd(q, k, v, True, 0.5)
+    assert o.shape == (2, 3, 10, 4) and lse.shape == (2, 3, 10)
+    o11, l11 = oracle.attention_fwd(q[1, 1], k[1, 1], v[1, 1], True, 0.5)
+    np.testing.assert_array_equal(o[1, 1], o11)
+    np.testing.assert_array_equal(lse[1, 1], l11)
+
+
+# --------------------------------------------------- independent library routine
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S,D", [(64, 64), (200, 128), (129, 64)])
+def test_oracle_matches_torch_cpu_float64(causal, S, D):
+    """torch's CPU attention kernel (float64) returns O and the natural-log LSE."""
+    shape = (2, 3, S, D)
+    q, k, v = _rand(shape, 24), _rand(shape, 25), _rand(shape, 26)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle.attention_fwd(q, k, v, causal, scale)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    to, tl = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(
+        tq, tk, tv, 0.0, causal, scale=scale)[:2]
+    np.testing.assert_allclose(o, to.numpy(), atol=1e-10)
+    np.testing.assert_allclose(lse, tl.numpy(), atol=1e-10)
+    to2 = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    np.testing.assert_allclose(o, to2.numpy(), atol=1e-10)
+
+
+def test_oracle_on_tiny_workload_16bit_inputs():
+    """The tiny workload's 16-bit inputs, decoded exactly, against torch float64."""
+    w = W.WORKLOADS["tiny"]
+    q, k, v = (W.decode(x, w.dtype) for x in W.make_inputs(w))
+    for causal in (False, True):
+        o, lse = oracle.attention_fwd(q, k, v, causal, w.scale)
+        to, tl = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(
+            *(torch.from_numpy(x) for x in (q, k, v)), 0.0, causal, scale=w.scale)[:2]
+        np.testing.assert_allclose(o, to.numpy(), atol=1e-11)
+        np.testing.assert_allclose(lse, tl.numpy(), atol=1e-11)
+
+
+# ------------------------------------------------ streaming algorithm (lagging max)
+
+def _lazy_golden():
+    with open(os.path.join(GOLDEN, "lazy_rescale.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("threshold", [0.0, 8.0])
+def test_online_lagging_max_reaches_definition(causal, threshold):
+    S, D = 300, 32
+    q, k, v = _rand((S, D), 27), _rand((S, D), 28), _rand((S, D), 29)
+    # a key ramp makes row maxima rise along the key axis
+    u = _rand((D,), 30)
+    u /= np.linalg.norm(u)
+    k = k + 0.05 * np.arange(S)[:, None] * u
+    q = q + u
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle.attention_fwd(q, k, v, causal, scale)
+    r = oracle.online_softmax_attention(q, k, v, causal, scale, block_n=64,
+                                        threshold_log2=threshold)
+    np.testing.assert_allclose(r["o"], o, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, atol=1e-12)
+    g = _lazy_golden()
+    if threshold == g["threshold_log2"]:
+        assert 1.0 < r["max_p"] <= g["p_upper_bound"]
+        assert r["min_history"] < g["history_when_rebased_at_most"]
+        assert r["rescales"].sum() > 0
+    else:
+        assert r["max_p"] <= 1.0 + 1e-15
+
+
+def test_online_threshold_reduces_rescales():
+    S, D = 512, 32
+    q, k, v = _rand((S, D), 31), _rand((S, D), 32), _rand((S, D), 33)
+    eager = oracle.online_softmax_attention(q, k, v, True, 0.2, 64, 0.0)["rescales"].sum()
+    lazy = oracle.online_softmax_attention(q, k, v, True, 0.2, 64, 8.0)["rescales"].sum()
+    assert eager > 0 and lazy < eager / 10
+
+
+# ------------------------------------------- planted mistakes must fail a pin
+
+def _pin_battery():
+    """Brute force, closed forms and the overflow case; True if all pass."""
+    try:
+        for S, D, causal in ((8, 4, False), (8, 4, True), (5, 3, True)):
+            q, k, v = _rand((S, D), 40 + S), _rand((S, D), 50 + S), _rand((S, D), 60 + S)
+            o, lse = oracle.attention_fwd(q, k, v, causal, 0.6)
+            ob, lb = oracle.attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), causal, 0.6)
+            if not (np.allclose(o, ob, atol=1e-12, rtol=0) and np.allclose(lse, lb, atol=1e-12, rtol=0)):
+                return False
+        for case in _golden_cases():
+            for causal in (False, True):
+                q, k, v = (np.array(case[n]) for n in ("q", "k", "v"))
+                exp = case["causal" if causal else "noncausal"]
+                o, lse = oracle.attention_fwd(q, k, v, causal, case["scale"])
+                if not np.allclose(o, [[_eval(x) for x in r] for r in exp["o"]], atol=1e-14, rtol=0):
+                    return False
+                if not np.allclose(lse, [_eval(x) for x in exp["lse"]], atol=1e-14, rtol=0):
+                    return False
+        # logits spread over thousands: any shift other than the row max
+        # overflows or underflows exp (the max only guards the numeric range)
+        q = _rand((6, 3), 70) * 2000
+        k = np.repeat(_rand((1, 3), 71), 6, axis=0)
+        v = _rand((6, 3), 72)
+        with np.errstate(all="ignore"):
+            o, lse = oracle.attention_fwd(q, k, v, True, 1.0)
+        mean = np.cumsum(v, axis=0) / np.arange(1, 7)[:, None]
+        return bool(np.allclose(o, mean, atol=1e-11) and np.all(np.isfinite(lse)))
+    except Exception:
+        return False
+
+
+_MUTANTS = {
+    "K and Q swapped in the logits": ("_logits", lambda q, k, scale: scale * (k @ q.T)),
+    "scale dropped": ("_logits", lambda q, k, scale: q @ k.T),
+    "mask hides the diagonal": ("_causal_mask", lambda x, rows: np.where(
+        np.arange(x.shape[1])[None, :] >= rows[:, None], -np.inf, x)),
+    "mask keeps the upper triangle": ("_causal_mask", lambda x, rows: np.where(
+        np.arange(x.shape[1])[None, :] < rows[:, None], -np.inf, x)),
+    "max over the wrong axis": ("_row_max", lambda x: x.max(axis=0)),
+    "max subtraction dropped": ("_row_max", lambda x: np.zeros(x.shape[0])),
+    "exponent sign flipped": ("_exp_shifted", lambda x, m: np.exp(-(x - m[:, None]))),
+    "base-2 exponential": ("_exp_shifted", lambda x, m: np.exp2(x - m[:, None])),
+    "sum over the wrong axis": ("_row_sum", lambda p: p.sum(axis=0)),
+    "normalisation dropped": ("_normalise", lambda acc, l: acc),
+    "lse log term dropped": ("_lse", lambda m, l: m),
+    "lse in log2": ("_lse", lambda m, l: m + np.log2(l)),
+    "lse sign flipped": ("_lse", lambda m, l: m - np.log(l)),
+}
+
+
+def test_pin_battery_passes_on_the_oracle():
+    assert _pin_battery()
+
+
+@pytest.mark.parametrize("name", sorted(_MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = _MUTANTS[name]
+    monkeypatch.setattr(OA, attr, fn)
+    assert not _pin_battery(), f"planted mistake not caught: {name}"

@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the fused attention forward.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark. It holds no attention arithmetic: it draws Gaussian Q/K/V from a
+seeded generator, rounds them to the 16-bit storage type, and decodes 16-bit
+storage back to float64 so that the oracle sees exactly the values the GPU
+receives.
+
+Workloads (all Q/K/V iid N(0,1), scale = 1/sqrt(D), layout [B, H, S, D]):
+
+====  ================================  =====  ======  ==========================
+name  shape (B, H, S, D)                dtype  causal  source of the shape
+====  ================================  =====  ======  ==========================
+tiny  1, 1, 128, 64                     fp16   both    small case for brute checks
+dec   1, 16, 1024, 64                   fp16   yes     causal decoder layer
+bat   10, 64, 1024, 64                  fp16   no      the Triton FA2 study's shape
+                                                       (hotdry.top, "FlashAttention
+                                                       的Triton性能考古学", grid section)
+long  2, 16, 8192, 128                  bf16   yes     long-context causal
+ramp  1, 8, 16384, 128                  bf16   yes     rescale stress (key ramp)
+====  ================================  =====  ======  ==========================
+
+Recipe: ``numpy.random.default_rng(seed)`` draws Q, then K, then V as float32
+``standard_normal``; the ``ramp`` workload then draws a unit vector ``u``
+(float64 normal, normalised), adds ``0.002*j*u`` to key row ``j`` and ``u`` to
+every query row, summed in float32.  Rounding to fp16 is numpy's
+round-to-nearest-even ``astype``; rounding to bf16 is the bit-exact
+round-to-nearest-even of the float32 pattern.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+# numeric codes shared with the C ABI's dtype enum (FA_F16 = 0, FA_BF16 = 1)
+DTYPE_CODE = {F16: 0, BF16: 1}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: str
+    causal: bool
+    seed: int
+    ramp: float = 0.0  # per-key additive ramp coefficient (0 = none)
+
+    @property
+    def scale(self) -> float:
+        """float32(1/sqrt(D)), the value passed to the kernel."""
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+    @property
+    def flops(self) -> float:
+        """Metric FLOPs: 4*B*H*S^2*D, halved when causal."""
+        f = 4.0 * self.B * self.H * self.S * self.S * self.D
+        return f / 2 if self.causal else f
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once and O written once (2 B/element) + LSE (4 B/row)."""
+        n = self.B * self.H * self.S * self.D
+        return 4 * 2 * n + 4 * self.B * self.H * self.S
+
+    def with_causal(self, causal: bool) -> "Workload":
+        return Workload(self.name, self.B, self.H, self.S, self.D, self.dtype,
+                        causal, self.seed, self.ramp)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 128, 64, F16, False, 1),
+    "tiny_causal": Workload("tiny_causal", 1, 1, 128, 64, F16, True, 1),
+    "dec": Workload("dec", 1, 16, 1024, 64, F16, True, 2),
+    "bat": Workload("bat", 10, 64, 1024, 64, F16, False, 3),
+    "long": Workload("long", 2, 16, 8192, 128, BF16, True, 4),
+    "ramp": Workload("ramp", 1, 8, 16384, 128, BF16, True, 5, ramp=0.002),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & 1
+    r = (u + np.uint32(0x7FFF) + lsb) >> 16
+    # NaN stays NaN (quiet); not produced by these generators
+    nan = np.isnan(x)
+    if nan.any():
+        r = np.where(nan, (u >> 16) | 0x40, r)
+    return r.astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (round to nearest even); uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def round_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F16:
+        return f32_to_f16_bits(x)
+    if dtype == BF16:
+        return f32_to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of 16-bit storage."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == F16:
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def make_inputs(w: Workload, ramp_override: float | None = None):
+    """Seeded Q, K, V as uint16 bit arrays of shape (B, H, S, D)."""
+    rng = np.random.default_rng(w.seed)
+    shape = (w.B, w.H, w.S, w.D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    ramp = w.ramp if ramp_override is None else ramp_override
+    if ramp:
+        u = rng.standard_normal(w.D)
+        u = u / np.linalg.norm(u)
+        j = np.arange(w.S, dtype=np.float64)
+        k += (ramp * j[:, None] * u[None, :]).astype(np.float32)
+        q += u.astype(np.float32)
+    return (round_bits(q, w.dtype), round_bits(k, w.dtype), round_bits(v, w.dtype))
+
+
+def random_bits(shape, dtype: str, seed: int, mean: float = 0.0, std: float = 1.0):
+    """Gaussian values rounded to 16-bit storage (for edge-case tests)."""
+    rng = np.random.default_rng(seed)
+    x = (mean + std * rng.standard_normal(shape)).astype(np.float32)
+    return round_bits(x, dtype)
+
