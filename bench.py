@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+
+One step = one fa_fwd call over one batch of the workload (the whole hot
+path: Q.K^T, mask, online softmax, P.V, epilogue). Inputs are seeded
+synthetic Gaussians already resident in HBM when timing starts. Prints one
+JSON line (rank 0) with the metric, a roofline entry for the kernel, and the
+CPU oracle timed on a bounded sample of the same workload.
+
+Default workload: B=2, H=16, S=8192, D=128, bf16, causal (the long-context
+configuration the metric is quoted on). FLOPs follow the metric:
+4*B*H*S^2*D, halved when causal.
+
+Extra modes (used to take profiles): --calibrate-copy runs plain device
+copies of a known size first (for scaling HBM byte counters);
+--no-cpu-baseline skips the oracle leg.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "attention fwd TFLOPS (B·H·S²·D·4, causal halved) + % of bf16 MFMA peak"
+PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA peak (published 2.5 PFLOP/s)
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_layout.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_long_hbm_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed counter profile, if it was
+    taken on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        import threadpoolctl
+        np.ones((64, 64)) @ np.ones((64, 64))
+        info = threadpoolctl.threadpool_info()
+        n = [i["num_threads"] for i in info if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w: W.Workload, qb, kb, vb, budget_s: float = 12.0):
+    """The float64 oracle on a random sample of query rows of the workload.
+
+    Rows are drawn uniformly over all heads and positions, processed in
+    batches until the time budget is spent; the metric FLOPs of the sample are
+    the workload's metric FLOPs times the fraction of rows done.
+    """
+    import oracle
+    rng = np.random.default_rng(123)
+    BH = w.B * w.H
+    rows_total = BH * w.S
+    done = 0
+    t0 = time.perf_counter()
+    heads = rng.permutation(BH)
+    batch = 64
+    i = 0
+    while time.perf_counter() - t0 < budget_s and i < len(heads) * 4:
+        bh = int(heads[i % len(heads)])
+        i += 1
+        b, h = divmod(bh, w.H)
+        rows = np.sort(rng.choice(w.S, size=batch, replace=False))
+        q = W.decode(qb[b, h], w.dtype)
+        k = W.decode(kb[b, h], w.dtype)
+        v = W.decode(vb[b, h], w.dtype)
+        oracle.attention_rows(q, k, v, rows, w.causal, w.scale)
+        done += batch
+    dt = time.perf_counter() - t0
+    tflops = w.flops * done / rows_total / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} random query rows of {rows_total} ({i} heads x {batch} rows, "
+                      f"float64 numpy, full key range per row) in {dt:.1f} s; value = metric "
+                      f"FLOPs x rows fraction / time",
+            "seconds": dt, "cpu": cpu_model()}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run plain 1 GiB device copies first (counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_16_amd as fa
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    fa.load()  # fails loudly if the HIP library is not built
+    qb, kb, vb = W.make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (qb, kb, vb))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)  # default priority
+    code = W.DTYPE_CODE[w.dtype]
+
+    def step():
+        fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  w.B, w.H, w.S, w.D, int(w.causal), w.scale, stream.cuda_stream, code)
+
+    torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)  # 1 GiB
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("calibrate-copy: 3 x 1 GiB device copies done", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back launches on `stream`, events on that stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    assert bool(torch.isfinite(lse).all()), "non-finite output"
+
+    # per-launch durations (events around each launch), median
+    per = []
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * min(args.steps, 20))]
+    for i in range(0, len(evs), 2):
+        evs[i].record(stream)
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    for i in range(0, len(evs), 2):
+        per.append(evs[i].elapsed_time(evs[i + 1]))
+    med_ms = float(np.median(per))
+
+    bytes_alg = w.algorithmic_bytes
+    print(f"Elapsed Time (total):      {gpu_ms / 1e3:.4f} seconds\n"
+          f"Average Time Per Step:     {ms_per_step:.4f} ms\n"
+          f"Compute Performance:       {tflops:.2f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of "
+          f"{PEAK_TFLOPS} peak)\n"
+          f"Memory Throughput:         {bytes_alg / (ms_per_step * 1e-3) / 1e9:.2f} GB/s "
+          f"(algorithmic bytes, decimal GB)\n"
+          f"Median single launch:      {med_ms:.4f} ms", file=sys.stderr, flush=True)
+
+    traffic = load_traffic(w.name)
+    roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_TFLOPS, "traffic": traffic,
+                "kernel": f"fa_fwd_kernel<{w.dtype},D={w.D},causal={int(w.causal)}>",
+                "flops_per_launch": w.flops, "avg_launch_ms": ms_per_step,
+                "median_launch_ms": med_ms, "algorithmic_bytes_per_launch": bytes_alg}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, qb, kb, vb)
+
+    out = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to 16-bit",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype} "
+                               f"{'causal' if w.causal else 'non-causal'}",
+                   "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": 100 * tflops / PEAK_TFLOPS,
+        "wall_s": wall,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

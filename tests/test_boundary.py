@@ -1,0 +1,132 @@
+"""The C-ABI boundary without a GPU: exported symbols, argument validation
+(which runs on the host before any HIP call) and the kernel's index math."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import exact_attention_16_amd as fa
+from exact_attention_16_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+
+OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == {"fa_fwd", "fa_fwd_f16", "fa_fwd_bf16", "fa_fwd_diag",
+                           "fa_fwd_tile", "fa_strerror", "fa_version"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                             text=True, check=True).stdout
+        exported = set(re.findall(r" T (fa_\w+)$", out, flags=re.M))
+        assert exported == _declared()
+
+
+def test_version_and_strerror():
+    assert fa.fa_version() == 100
+    for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG):
+        assert fa.fa_strerror(st) and fa.fa_strerror(st) != "unknown status"
+    assert fa.fa_strerror(12345) == "unknown status"
+
+
+def test_tile_query():
+    assert fa.fa_fwd_tile(128, 2, 16, 8192) == (128, 64, 256, 2 * 16 * 64)
+    assert fa.fa_fwd_tile(64, 10, 64, 1024) == (128, 128, 256, 640 * 8)
+    assert fa.fa_fwd_tile(64, 1, 1, 129)[3] == 2
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_tile(96)
+
+
+# fake, 16-byte aligned, non-overlapping device addresses: validation never
+# dereferences them and rejects every case below before any HIP call
+N = 1 << 30
+Q, K, V, O, L = (0x10000000000 + i * 4 * N for i in range(5))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, S=100, D=64, causal=1, scale=0.125,
+            stream=None, dtype=0)
+
+
+def _call(**kw):
+    a = dict(GOOD, **kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"],
+                     a["causal"], a["scale"], a["stream"], a["dtype"], check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL),
+    (dict(lse=0), NULL),
+    (dict(B=-1), DIM), (dict(H=-2), DIM), (dict(S=-5), DIM), (dict(S=(1 << 30) + 1), DIM),
+    (dict(B=1 << 20, H=1 << 10, S=1 << 12), DIM),
+    (dict(D=96), UNSUP), (dict(D=0), UNSUP), (dict(D=256), UNSUP), (dict(dtype=2), UNSUP),
+    (dict(dtype=-1), UNSUP),
+    (dict(q=Q + 8), ALIGN), (dict(o=O + 2), ALIGN), (dict(lse=L + 4), ALIGN),
+    (dict(scale=0.0), SCALE), (dict(scale=-0.1), SCALE), (dict(scale=float("nan")), SCALE),
+    (dict(scale=float("inf")), SCALE),
+    (dict(o=Q), ALIAS), (dict(o=K + 1024), ALIAS), (dict(lse=V + 64), ALIAS),
+    (dict(lse=O + 16), ALIAS), (dict(o=V - 16), ALIAS),
+    (dict(causal=2), ARG), (dict(causal=-1), ARG),
+])
+def test_validation_rejects(kw, expect):
+    assert _call(**kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(S=0),
+                                dict(S=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_empty_problem_is_a_noop(kw):
+    assert _call(**kw) == OK
+
+
+def test_typed_wrappers_validate_the_same_way():
+    a = GOOD
+    assert fa.fa_fwd_f16(a["q"], a["k"], a["v"], 0, a["lse"], 1, 1, 8, 64, 0, 0.1, None,
+                         check=False) == NULL
+    assert fa.fa_fwd_bf16(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 8, 64, 0, -1.0, None,
+                          check=False) == SCALE
+    assert fa.fa_fwd_bf16(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 0, 64, 0, 0.1, None,
+                          check=False) == OK
+
+
+def test_diag_validation():
+    a = GOOD
+    args = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 8, 64, 0, 0.1, None, 0)
+    assert fa.fa_fwd_diag(*args, 3, 0x20000000000, check=False) == ARG
+    assert fa.fa_fwd_diag(*args, 8, 0, check=False) == NULL
+    assert fa.fa_fwd_diag(*args, 0, 0x20000000004, check=False) == ALIGN
+    e = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 0, 64, 0, 0.1, None, 0)
+    assert fa.fa_fwd_diag(*e, 8, 0x20000000000, check=False) == OK
+
+
+def test_error_raises_with_name():
+    with pytest.raises(fa.FaError, match="FA_ERR_NULL"):
+        fa.fa_fwd(0, 0, 0, 0, 0, 1, 1, 8, 64, 0, 0.1, None, 0)
+
+
+def test_kernel_index_math_on_host(tmp_path):
+    """Bounds, exact LDS coverage, operand element mapping, work decomposition
+    and LDS bank-conflict degree of every access the kernel makes."""
+    gxx = shutil.which("g++") or shutil.which("c++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = tmp_path / "layout_check"
+    subprocess.run([gxx, "-std=c++17", "-O2", "-o", str(exe),
+                    os.path.join(ROOT, "tests", "host", "layout_check.cpp")], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    print(r.stdout)
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), r.stdout

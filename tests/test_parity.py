@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle
+on the same seeded 16-bit inputs.
+
+Tolerance: max |O_gpu - O_oracle| <= 5e-3 (fp16) / 2e-2 (bf16) over every
+compared element, and max |lse_gpu - lse_oracle| <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_16_amd as fa
+import oracle
+import workloads as W
+from gpu_util import (LSE_TOL, O_TOL, compare_rows, o_to_f64, run, sample_rows, to_dev,
+                      device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(msg):
+    print(msg, flush=True)
+
+
+def _check_full(qb, kb, vb, dtype, causal, scale, tag):
+    o, lse = run(qb, kb, vb, dtype, causal, scale)
+    og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    B, H, S, _ = qb.shape
+    eo, el = compare_rows(qb, kb, vb, dtype, causal, scale, og, lg,
+                          [((b, h), np.arange(S)) for b in range(B) for h in range(H)])
+    _banner(f"{tag}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    assert eo <= O_TOL[dtype], (tag, eo)
+    assert el <= LSE_TOL, (tag, el)
+    return og, lg
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_workload(causal):
+    w = W.WORKLOADS["tiny"].with_causal(causal)
+    _banner(f"tiny causal={causal}")
+    _check_full(*W.make_inputs(w), w.dtype, causal, w.scale, f"tiny causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 7, 64, 129, 300])
+def test_small_shapes_all_rows(S, causal, D, dtype):
+    """Several Q and KV tiles, ragged tails, tiny S; every output compared."""
+    shape = (2, 3, S, D)
+    seed = 1000 + S * 4 + D + (dtype == W.BF16) * 2 + causal
+    qb, kb, vb = (W.random_bits(shape, dtype, seed + i) for i in range(3))
+    _check_full(qb, kb, vb, dtype, causal, 1.0 / math.sqrt(D),
+                f"S={S} D={D} {dtype} causal={causal}")
+
+
+# full-size workloads, sampled rows (the oracle computes each row on its own)
+_SAMPLES = {"dec": (None, None), "bat": (8, 24), "long": (None, 96), "ramp": (None, 96)}
+
+
+@pytest.mark.parametrize("name", ["dec", "bat", "long", "ramp"])
+def test_workload_full_size(name):
+    w = W.WORKLOADS[name]
+    _banner(f"workload {name}: B={w.B} H={w.H} S={w.S} D={w.D} {w.dtype} causal={w.causal}")
+    qb, kb, vb = W.make_inputs(w)
+    o, lse = run(qb, kb, vb, w.dtype, w.causal, w.scale)
+    og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    full_heads, nrows = _SAMPLES[name]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    plan = []
+    for n, bh in enumerate(heads):
+        if nrows is None or (full_heads is not None and n % max(1, len(heads) // full_heads) == 0):
+            plan.append((bh, np.arange(w.S)))
+        else:
+            plan.append((bh, sample_rows(w.S, nrows, seed=n)))
+    eo, el = compare_rows(qb, kb, vb, w.dtype, w.causal, w.scale, og, lg, plan)
+    _banner(f"workload {name}: rows compared={sum(len(r) for _, r in plan)} "
+            f"max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= O_TOL[w.dtype] and el <= LSE_TOL
+
+
+def test_long_context_max_rows():
+    """One head at S=65536 (the largest size tested), causal bf16, sampled rows."""
+    shape, dt = (1, 1, 65536, 128), W.BF16
+    qb, kb, vb = (W.random_bits(shape, dt, 77 + i) for i in range(3))
+    o, lse = run(qb, kb, vb, dt, True, 128 ** -0.5)
+    og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    eo, el = compare_rows(qb, kb, vb, dt, True, 128 ** -0.5, og, lg,
+                          [((0, 0), sample_rows(65536, 48, seed=5))])
+    _banner(f"S=65536: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= O_TOL[dt] and el <= LSE_TOL
+
+
+# ------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("D", [64, 128])
+def test_constant_v_and_causal_row0(dtype, D):
+    S = 257
+    qb = W.random_bits((1, 2, S, D), dtype, 5)
+    kb = W.random_bits((1, 2, S, D), dtype, 6)
+    vb = W.round_bits(np.full((1, 2, S, D), 0.8125, np.float32), dtype)
+    og, lg = _check_full(qb, kb, vb, dtype, True, D ** -0.5, f"constV D={D} {dtype}")
+    assert np.abs(og - 0.8125).max() <= O_TOL[dtype]
+    # causal row 0 sees only key 0: O = V[0] (exactly representable), lse = scale*q0.k0
+    vb2 = W.random_bits((1, 2, S, D), dtype, 7)
+    o, lse = run(qb, kb, vb2, dtype, True, D ** -0.5)
+    og2 = o_to_f64(o)
+    np.testing.assert_array_equal(og2[:, :, 0], W.decode(vb2[:, :, 0], dtype))
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_identical_keys_closed_form(dtype):
+    """All keys equal: O_i = mean of visible V rows, lse_i = scale*q_i.k + ln(i+1)."""
+    S, D = 200, 128
+    qb = W.random_bits((1, 1, S, D), dtype, 8)
+    k1 = W.random_bits((1, 1, 1, D), dtype, 9)
+    kb = np.repeat(k1, S, axis=2)
+    vb = W.random_bits((1, 1, S, D), dtype, 10)
+    o, lse = run(qb, kb, vb, dtype, True, D ** -0.5)
+    v = W.decode(vb[0, 0], dtype)
+    mean = np.cumsum(v, axis=0) / np.arange(1, S + 1)[:, None]
+    q = W.decode(qb[0, 0], dtype)
+    k = W.decode(k1[0, 0, 0], dtype)
+    lse_ref = float(np.float32(D ** -0.5)) * (q @ k) + np.log(np.arange(1, S + 1))
+    assert np.abs(o_to_f64(o)[0, 0] - mean).max() <= O_TOL[dtype]
+    assert np.abs(lse.cpu().numpy()[0, 0] - lse_ref).max() <= LSE_TOL
+
+
+def test_key_shift_moves_lse_only():
+    """K += w shifts row i's logits by scale*q_i.w: O unchanged, lse shifted."""
+    S, D, dt = 384, 64, W.F16
+    q = W.decode(W.random_bits((1, 1, S, D), dt, 11), dt)
+    # keys on a 1/64 grid within [-6, 6]: k and k + w are both exact in fp16
+    k = np.clip(np.round(W.decode(W.random_bits((1, 1, S, D), dt, 12), dt) * 64) / 64, -6, 6)
+    vb = W.random_bits((1, 1, S, D), dt, 13)
+    w = np.zeros(D)
+    w[:4] = 2.0  # exactly representable shift: k + w stays exact in fp16 here
+    kb1 = W.round_bits(k.astype(np.float32), dt)
+    kb2 = W.round_bits((k + w).astype(np.float32), dt)
+    assert np.array_equal(W.decode(kb2, dt) - W.decode(kb1, dt), np.broadcast_to(w, k.shape))
+    qb = W.round_bits(q.astype(np.float32), dt)
+    o1, l1 = run(qb, kb1, vb, dt, False, 0.125)
+    o2, l2 = run(qb, kb2, vb, dt, False, 0.125)
+    assert np.abs(o_to_f64(o1) - o_to_f64(o2)).max() <= O_TOL[dt]
+    shift = 0.125 * (q[0, 0] @ w)
+    assert np.abs((l2.cpu().numpy() - l1.cpu().numpy())[0, 0] - shift).max() <= 2 * LSE_TOL
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_large_logits_do_not_overflow(dtype):
+    """Logits of several hundred: the lagging base keeps every p in (0, 256]."""
+    S, D = 256, 64
+    qb = W.random_bits((1, 2, S, D), dtype, 14, std=6.0)
+    kb = W.random_bits((1, 2, S, D), dtype, 15, std=6.0)
+    vb = W.random_bits((1, 2, S, D), dtype, 16)
+    _check_full(qb, kb, vb, dtype, False, 0.125, f"large logits {dtype}")
+
+
+# -------------------------------------------------------- lazy vs eager rescale
+
+def _diag(qb, kb, vb, dtype, causal, scale, thr):
+    q, k, v = (to_dev(x, dtype) for x in (qb, kb, vb))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device())
+    ev = torch.zeros(1, dtype=torch.int64, device=device())
+    B, H, S, D = q.shape
+    fa.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   B, H, S, D, causal, scale, torch.cuda.current_stream().cuda_stream,
+                   W.DTYPE_CODE[dtype], thr, ev.data_ptr())
+    torch.cuda.synchronize()
+    return o_to_f64(o), lse.cpu().numpy().astype(np.float64), int(ev.item())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_lagging_and_eager_rescale_both_match(D):
+    """Threshold 8 (production) and 0 (eager) both meet tolerance on a steep
+    key ramp; the lag cuts rescale events; event counts track the float64
+    model of the same algorithm with the same KV tile size."""
+    dt = W.BF16
+    w = W.Workload("steep", 1, 2, 2048, D, dt, True, 21, ramp=0.05)
+    qb, kb, vb = W.make_inputs(w)
+    res = {thr: _diag(qb, kb, vb, dt, True, w.scale, thr) for thr in (8, 0)}
+    plan = [((0, h), sample_rows(w.S, 128, seed=h)) for h in range(w.H)]
+    for thr, (og, lg, ev) in res.items():
+        eo, el = compare_rows(qb, kb, vb, dt, True, w.scale, og, lg, plan)
+        _banner(f"D={D} threshold={thr}: events={ev} max|dO|={eo:.3e} max|dlse|={el:.3e}")
+        assert eo <= O_TOL[dt] and el <= LSE_TOL
+    lazy, eager = res[8][2], res[0][2]
+    assert 0 < lazy < eager
+    # production result equals fa_fwd bit for bit (same arithmetic, counter aside)
+    o, lse = run(qb, kb, vb, dt, True, w.scale)
+    np.testing.assert_array_equal(o_to_f64(o), res[8][0])
+    # the float64 model of the algorithm, same KV tile size
+    bn = fa.fa_fwd_tile(D)[1]
+    model = {8: 0, 0: 0}
+    for h in range(w.H):
+        q, k, v = (W.decode(x[0, h], dt) for x in (qb, kb, vb))
+        for thr in (8, 0):
+            model[thr] += int(oracle.online_softmax_attention(
+                q, k, v, True, w.scale, block_n=bn, threshold_log2=thr)["rescales"].sum())
+    _banner(f"D={D} model events: lazy={model[8]} eager={model[0]}")
+    for thr in (8, 0):
+        gpu = res[thr][2]
+        assert abs(gpu - model[thr]) <= max(4, 0.02 * model[thr]), (thr, gpu, model[thr])
+
+
+# ---------------------------------------------------- hygiene of the launch
+
+def test_deterministic():
+    shape, dt = (1, 4, 2048, 128), W.BF16
+    qb, kb, vb = (W.random_bits(shape, dt, 30 + i) for i in range(3))
+    o1, l1 = run(qb, kb, vb, dt, True, 128 ** -0.5)
+    o2, l2 = run(qb, kb, vb, dt, True, 128 ** -0.5)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_no_writes_outside_outputs(D):
+    """Outputs embedded in guard bands: the kernel writes only O and lse."""
+    B, H, S, dt = 1, 3, 200, W.F16
+    qb, kb, vb = (W.random_bits((B, H, S, D), dt, 40 + i) for i in range(3))
+    q, k, v = (to_dev(x, dt) for x in (qb, kb, vb))
+    n, nl, g = B * H * S * D, B * H * S, 4096
+    obuf = torch.full((n + 2 * g,), 7.0, dtype=torch.float16, device=device())
+    lbuf = torch.full((nl + 2 * g,), -3.0, dtype=torch.float32, device=device())
+    o = obuf[g:g + n]
+    lse = lbuf[g:g + nl]
+    fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, S, D,
+              1, D ** -0.5, torch.cuda.current_stream().cuda_stream, fa.FA_F16)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:g] == 7.0) and torch.all(obuf[g + n:] == 7.0)
+    assert torch.all(lbuf[:g] == -3.0) and torch.all(lbuf[g + nl:] == -3.0)
+    assert torch.all(torch.isfinite(o)) and torch.all(torch.isfinite(lse))
+
+
+def test_side_stream_and_typed_wrappers():
+    shape, dt = (2, 2, 320, 64), W.BF16
+    qb, kb, vb = (W.random_bits(shape, dt, 50 + i) for i in range(3))
+    ref_o, ref_l = run(qb, kb, vb, dt, True, 0.125)
+    s = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(s):
+        o, l = run(qb, kb, vb, dt, True, 0.125, stream=s)
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    q, k, v = (to_dev(x, dt) for x in (qb, kb, vb))
+    o2 = torch.empty_like(q)
+    l2 = torch.empty_like(ref_l)
+    fa.fa_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(), l2.data_ptr(),
+                   *shape, 1, 0.125, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, ref_o) and torch.equal(l2, ref_l)
+
+
+def test_empty_inputs_launch_nothing():
+    z = torch.empty((0,), dtype=torch.float16, device=device())
+    assert fa.fa_fwd(z.data_ptr(), z.data_ptr(), z.data_ptr(), z.data_ptr(), 0, 1, 4, 0, 64, 1,
+                     0.125, torch.cuda.current_stream().cuda_stream, fa.FA_F16) == 0
+    torch.cuda.synchronize()
