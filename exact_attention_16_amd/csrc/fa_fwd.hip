@@ -1,28 +1,34 @@
 // Fused attention forward for AMD Instinct MI355X (gfx950, CDNA4).
 //
 // One work-group = 4 waves = one Q tile of 128 query rows of one (batch,
-// head); each wave owns 32 query rows for the whole kernel. Per KV tile:
+// head); each wave owns 32 query rows for the whole kernel, with its Q rows
+// held in registers as MFMA operands. K and V stream through LDS in tiles of
+// 64 keys, two LDS buffers each.
 //
-//   1. K tile and V^T tile of the next KV tile are fetched from HBM into
-//      registers (16-byte loads, consecutive lanes on consecutive bytes)
-//      while the current tile is consumed from LDS (double buffer).
-//   2. S^T = K Q^T on v_mfma_f32_32x32x16 (raw dot products in fp32; the
-//      scale is folded into the exponent). Q stays in registers as MFMA
-//      operands for the whole kernel; K rows are read from LDS as 16-byte
-//      operand fragments, so K never needs a transpose.
-//   3. Causal: tiles wholly above the diagonal are never visited, tiles
-//      wholly below are not masked; only tiles that straddle the diagonal
-//      (or the ragged end) compare indices.
-//   4. Online softmax in base 2 with a lagging running max b: the tile max
-//      is exchanged between the two lanes of a row with v_permlane32_swap;
-//      b moves only when the candidate exceeds b + THR, and only then is the
-//      O accumulator rescaled (wave-uniform branch on a ballot).
-//      p = 2^(s*c - b) with c = scale*log2(e); row sums accumulate the
-//      unrounded fp32 p.
-//   5. O^T += V^T P^T on v_mfma_f32_32x32x16: P goes from the S accumulator
-//      to the MFMA operand inside the lane; V^T fragments come from LDS.
-//   6. Epilogue: one division per row, O rounded once to the 16-bit type,
-//      lse = ln2 * (b + log2(l)).
+// Data movement: K and V tiles go from HBM to LDS by buffer loads with the
+// LDS bit (direct DMA, 16 bytes per lane; no staging registers, no VALU),
+// whose range check zero-fills rows past the end of the sequence. K is read
+// back as 16-byte S^T operand fragments (no transpose); V^T operand
+// fragments come from the row-major V tile through ds_read_b64_tr_b16,
+// which transposes in the LDS crossbar. Both tiles are XOR-swizzled per row
+// so that the operand reads are free of bank conflicts.
+//
+// Per KV tile j, each wave runs a three-stage register pipeline in one
+// scheduling block, so that the matrix cores and the vector ALU overlap:
+//   S(j+1) = K(j+1) Q^T      (MFMA, v_mfma_f32_32x32x16)
+//   O^T   += V(j-1)^T P(j-1)^T (MFMA)
+//   softmax(S(j)) -> P(j)    (VALU: max, exp2, sum, convert)
+// followed, only when some row's running max moved, by the O rescale.
+//
+// Softmax: base 2 with a lagging running base b per row (log2 units of the
+// scaled logit). The tile max of the raw dot products is exchanged between
+// the two lanes of a row with v_permlane32_swap; b moves only when the
+// candidate exceeds b + THR, with history factor 2^(b_old - b_new); p =
+// 2^(s*c - b) with c = scale*log2(e), so p <= 2^THR. Row sums accumulate the
+// unrounded fp32 p; P is rounded once to the input type for the MFMA. The
+// O rescale is skipped, wave-uniformly, unless a ballot finds a row with
+// history < 1. Causal tiles wholly above the diagonal are never visited;
+// only tiles crossing the diagonal or the ragged end compare indices.
 //
 // Method sources: exact attention softmax(QK^T/sqrt(d)+mask)V with a
 // lower-triangle causal mask (xdnf.cn, "CUDA手写masked multi-head attention
@@ -30,8 +36,9 @@
 // normalisation and the (Q tile, head) grid (hotdry.top, "FlashAttention的
 // Triton性能考古学", "核心算法回顾" and "FlashAttention v2"); the conditional
 // rescale with a lag of 8 and p in (0, 256], the warp-vote skip of the
-// rescale and the rescale done by the softmax workers themselves
-// (hjcheng0602.cn, "Flash Attention CUDA Kernel 优化 ... G6", V41 and V44).
+// rescale, the rescale done by the softmax workers themselves, and issuing
+// the next tile's Q.K^T ahead of the current P.V (hjcheng0602.cn, "Flash
+// Attention CUDA Kernel 优化 ... G6", V39, V41 and V44).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -45,6 +52,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -52,6 +60,13 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
+// Word 3 of a raw (untyped, stride 0) gfx9 buffer descriptor.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <int N> struct IC { static constexpr int value = N; };
+template <int P, class X> __device__ __forceinline__ X& pick(X& one, X& zero) {
+  if constexpr (P != 0) return one; else return zero;
+}
 
 template <typename T> struct Ops;
 
@@ -91,7 +106,22 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+// Raw buffer descriptor over `bytes` bytes at `base`. A macro rather than a
+// function: a function or lambda returning the descriptor type makes the
+// host compilation pass drop the kernel launch stubs.
+#define FA_RSRC(base, bytes) \
+  __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>((const void*)(base)), 0, (int)(bytes), kBufferWord3)
+
+// LDS pointers stay in address space 3 from the point where each shared
+// array is declared (a cast of a generic pointer to address space 3 would
+// make the host compilation pass drop the kernel launch stubs).
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ u32x4 lds16(const lds_char* p) { return *(lds_u32x4*)p; }
+
+template <int D> struct Pipe { static constexpr bool three = D == 64; };
 
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 __global__ void __launch_bounds__(kThreads)
@@ -99,13 +129,30 @@ __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               T* __restrict__ O, float* __restrict__ LSE, int BH, int S, int nqt, float c,
               unsigned long long* __restrict__ events) {
-  using L = Lds<D>;
-  constexpr int BN = L::BN;
+  using TL = Tile<D>;
+  constexpr bool P3 = Pipe<D>::three;
+  // V^T operand: two transposed 8-byte reads (keys +0..3 and +4..7)
+  auto lds_tr_pair = [](const lds_char* p, uint32_t second) -> u32x4 {
+    const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + second));
+    const u32x2 x = __builtin_bit_cast(u32x2, x0), y = __builtin_bit_cast(u32x2, x1);
+    return (u32x4){x[0], x[1], y[0], y[1]};
+  };
+  constexpr int BN = TL::BN;
   constexpr int NKB = BN / 32;   // 32-key blocks per KV tile
-  constexpr int NDC = D / 16;    // 16-wide d chunks (QK^T contraction steps)
+  constexpr int NDC = D / 16;    // Q.K^T contraction steps (16 d each)
   constexpr int NDB = D / 32;    // 32-row d blocks of O^T
-  constexpr int NKC = BN / 16;   // 16-key chunks (P.V contraction steps)
-  __shared__ __attribute__((aligned(1024))) char smem[L::totalBytes];
+  constexpr int NKC = BN / 16;   // P.V contraction steps (16 keys each)
+  constexpr int DPW = TL::dmaPerWave;
+  constexpr uint32_t RB = TL::rowBytes;
+  __shared__ __attribute__((aligned(1024))) char ks0[TL::bytes];
+  __shared__ __attribute__((aligned(1024))) char ks1[TL::bytes];
+  __shared__ __attribute__((aligned(1024))) char vs0[TL::bytes];
+  __shared__ __attribute__((aligned(1024))) char vs1[TL::bytes];
+  lds_char* const lk0 = (lds_char*)ks0;
+  lds_char* const lk1 = (lds_char*)ks1;
+  lds_char* const lv0 = (lds_char*)vs0;
+  lds_char* const lv1 = (lds_char*)vs1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,23 +163,30 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   int qt, bh;
   block_to_tile(blockIdx.x, BH, nqt, CAUSAL, &qt, &bh);
   const size_t head = (size_t)bh * (size_t)S * D;
-  Q += head;
-  K += head;
-  V += head;
-  O += head;
-  LSE += (size_t)bh * S;
+  const T* Kh = K + head;
+  const T* Vh = V + head;
+  const uint32_t head_bytes = (uint32_t)S * RB;
+  const auto rq = FA_RSRC(Q + head, head_bytes);
+  const auto ro = FA_RSRC(O + head, head_bytes);
+  const auto rl = FA_RSRC(LSE + (size_t)bh * S, (uint32_t)S * 4u);
 
   const int q0w = qt * kBM + wave * kRowsPerWave;  // first row of this wave
   const int qrow = q0w + i32;                      // this lane's row
-  const int qrow_c = qrow < S ? qrow : S - 1;
-  const int ntiles = (tile_kv_end(qt, S, CAUSAL) + BN - 1) / BN;
-  const int wkv_end = wave_kv_end(q0w, S, CAUSAL);
   const bool wave_live = q0w < S;
+  const int ntiles = (tile_kv_end(qt, S, CAUSAL) + BN - 1) / BN;
+  const int nw = wave_live ? (wave_kv_end(q0w, S, CAUSAL) + BN - 1) / BN : 0;
 
-  // Q operand fragments: lane holds q[qrow, 16*j + 8*hh + 0..7]
+  // Q operand fragments (rows past S read as zeros)
   u32x4 qf[NDC];
 #pragma unroll
-  for (int j = 0; j < NDC; ++j) qf[j] = ld16(Q + q_frag_off<D>(qrow_c, j, hh));
+  for (int j = 0; j < NDC; ++j)
+    qf[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_frag_off<D>(qrow, j, hh), 0, 0);
+
+  // per-lane LDS / DMA base offsets; the rest are XOR / immediate offsets
+  const uint32_t koff0 = k_read_off<D>(0, 0, lane);
+  const uint32_t voff0 = v_tr_off<D>(0, 0, 0, lane);
+  const uint32_t kdo0 = dma_src_k<D>(wave, 0, lane);
+  const uint32_t vdo0 = dma_src_v<D>(wave, 0, lane);
 
   f32x16 o[NDB];
 #pragma unroll
@@ -141,147 +195,198 @@ fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   float lsum = 0.f;     // this lane's partial row sum (its k-half of the keys)
   unsigned n_events = 0;
 
-  u32x4 kreg[L::kChunksPerThread];
-  u32x4 vreg[L::vUnitsPerThread][4];
-
-  auto gload = [&](int t) {
+  // ---- building blocks --------------------------------------------------
+  auto dma_k = [&](lds_char* dst, int t) {
     const int kv0 = t * BN;
+    const auto r = FA_RSRC(Kh + (size_t)kv0 * D, (uint32_t)(S - kv0) * RB);
 #pragma unroll
-    for (int n = 0; n < L::kChunksPerThread; ++n) {
-      int key, ch;
-      k_stage_map<D>(tid + n * kThreads, &key, &ch);
-      kreg[n] = ld16(K + kv_chunk_off<D>(kv_row(kv0, key, S), ch));
-    }
-#pragma unroll
-    for (int n = 0; n < L::vUnitsPerThread; ++n) {
-      int kg, dc;
-      v_stage_map<D>(tid + n * kThreads, &kg, &dc);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        vreg[n][q4] = ld16(V + kv_chunk_off<D>(kv_row(kv0, 4 * kg + q4, S), dc));
+    for (int i = 0; i < DPW; ++i)
+    {
+      // (the LDS pointer goes through a local: written inline as the builtin's
+      // argument, the host compilation pass drops the kernel launch stubs)
+      lds_char* const lp = dst + dma_lds_k<D>(wave, i);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, kdo0 + i * kDmaStrideK, 0, 0, 0);
     }
   };
-  auto swrite = [&](int stage) {
-    char* sb = smem + stage * L::stageBytes;
+  auto dma_v = [&](lds_char* dst, int t) {
+    const int kv0 = t * BN;
+    const auto r = FA_RSRC(Vh + (size_t)kv0 * D, (uint32_t)(S - kv0) * RB);
 #pragma unroll
-    for (int n = 0; n < L::kChunksPerThread; ++n)
-      *(u32x4*)(sb + k_write_off<D>(tid + n * kThreads)) = kreg[n];
-    // V is written transposed: 4 keys of one d packed as 8 bytes.
-#pragma unroll
-    for (int n = 0; n < L::vUnitsPerThread; ++n) {
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w0 = __builtin_amdgcn_perm(vreg[n][1][dd >> 1], vreg[n][0][dd >> 1], sel);
-        const uint32_t w1 = __builtin_amdgcn_perm(vreg[n][3][dd >> 1], vreg[n][2][dd >> 1], sel);
-        *(u32x2*)(sb + vt_write_off<D>(tid + n * kThreads, dd)) = (u32x2){w0, w1};
-      }
+    for (int i = 0; i < DPW; ++i)
+    {
+      // (the LDS pointer goes through a local: written inline as the builtin's
+      // argument, the host compilation pass drops the kernel launch stubs)
+      lds_char* const lp = dst + dma_lds_v<D>(wave, i);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, vdo0 + i * kDmaStrideV, 0, 0, 0);
     }
   };
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    const int kv0 = t * BN;
-    if (t + 1 < ntiles) gload(t + 1);
-
-    if (wave_live && kv0 < wkv_end) {
-      const char* sb = smem + stage * L::stageBytes;
-
-      // ---- S^T = K Q^T (raw dot products) --------------------------------
-      f32x16 s[NKB];
+  auto qk = [&](f32x16 (&s)[NKB], const lds_char* kt) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = (f32x16){};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = (f32x16){};
 #pragma unroll
-        for (int j = 0; j < NDC; ++j)
-          s[kb] = Ops<T>::mfma(ld16(sb + k_read_off<D>(kb, j, lane)), qf[j], s[kb]);
-      }
-
-      // ---- mask: only tiles crossing the diagonal or the ragged end ------
-      const bool need_mask = (CAUSAL && kv0 + BN - 1 > q0w) || (kv0 + BN > S);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + acc_key32(r, hh);
-            const bool vis = key < S && (!CAUSAL || key <= qrow);
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
-          }
-      }
-
-      // ---- running max with lag (conditional rescale) ---------------------
-      float mx = s[0][0];
+    for (int j = 0; j < NDC; ++j) {
+      const lds_char* base = kt + (koff0 ^ (uint32_t)(j << 5));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = max_xor32(mx);
-      const float cand = fmaxf(b, mx * c);
-      float hist = 1.f;
-      if (cand > b + (float)THR) {
-        hist = __builtin_amdgcn_exp2f(b - cand);  // 2^(b_old - b_new); 0 on the first tile
-        b = cand;
-      }
-      if (DIAG && t > 0 && hh == 0 && qrow < S && hist < 1.f) ++n_events;
-      // rare path: some row of the wave moved its base -> rescale O rows
-      if (t > 0 && __builtin_amdgcn_ballot_w64(hist < 1.f) != 0) {
-        lsum *= hist;
-#pragma unroll
-        for (int j = 0; j < NDB; ++j) o[j] *= hist;
-      }
-      const float nb = (b == -INFINITY) ? 0.f : -b;  // fully hidden row: p = 0
-
-      // ---- p = 2^(s*c - b), row sum (fp32, unrounded), pack P -------------
-      u32x4 pf[NKC];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + e], c, nb));
-            lsum += p[e];
-          }
-          pf[2 * kb + g] = (u32x4){Ops<T>::pack2(p[0], p[1]), Ops<T>::pack2(p[2], p[3]),
-                                   Ops<T>::pack2(p[4], p[5]), Ops<T>::pack2(p[6], p[7])};
-        }
-
-      // ---- O^T += V^T P^T -------------------------------------------------
-#pragma unroll
-      for (int j = 0; j < NDB; ++j)
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-          o[j] = Ops<T>::mfma(ld16(sb + vt_read_off<D>(j, kc, lane)), pf[kc], o[j]);
+        s[kb] = Ops<T>::mfma(lds16(base + kb * 32 * RB), qf[j], s[kb]);
     }
-
-    if (t + 1 < ntiles) swrite(stage ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: normalise once, write O and lse ---------------------------
-  const float ltot = sum_xor32(lsum);
-  if (wave_live && qrow < S) {
-    const float inv = 1.f / ltot;
+  };
+  auto pv = [&](const u32x4 (&p)[NKC], const lds_char* vt) {
 #pragma unroll
-    for (int j = 0; j < NDB; ++j)
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int jd = 0; jd < NDB; ++jd)
+        o[jd] = Ops<T>::mfma(lds_tr_pair(vt + (voff0 ^ (uint32_t)(jd << 6)) + kc * 16 * RB, 4 * RB),
+                             p[kc], o[jd]);
+  };
+  auto mask = [&](f32x16 (&s)[NKB], int kv0) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * kb + acc_key32(r, hh);
+        const bool vis = key < S && (!CAUSAL || key <= qrow);
+        s[kb][r] = vis ? s[kb][r] : -INFINITY;
+      }
+  };
+  // running max with lag, p = 2^(s*c - b), row sum, P packed; returns history
+  auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&p)[NKC]) -> float {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_xor32(mx);
+    const float cand = fmaxf(b, mx * c);
+    const bool rebase = cand > b + (float)THR;
+    const float hist = rebase ? __builtin_amdgcn_exp2f(b - cand) : 1.f;  // 0 on the first tile
+    b = rebase ? cand : b;
+    const float nb = (b == -INFINITY) ? 0.f : -b;  // fully hidden row: p = 0
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const f32x16& a = o[j];
-        const int r0 = 8 * g;
-        u32x4 w = {Ops<T>::pack2(a[r0 + 0] * inv, a[r0 + 1] * inv),
-                   Ops<T>::pack2(a[r0 + 2] * inv, a[r0 + 3] * inv),
-                   Ops<T>::pack2(a[r0 + 4] * inv, a[r0 + 5] * inv),
-                   Ops<T>::pack2(a[r0 + 6] * inv, a[r0 + 7] * inv)};
-        // accumulator element r0+e of lane (i32, hh) is d = 32j + 16g + 8hh + e
-        *(u32x4*)(O + o_frag_off<D>(qrow, j, g, hh)) = w;
+        float e[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          e[x] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + x], c, nb));
+          ls += e[x];
+        }
+        p[2 * kb + g] = (u32x4){Ops<T>::pack2(e[0], e[1]), Ops<T>::pack2(e[2], e[3]),
+                                Ops<T>::pack2(e[4], e[5]), Ops<T>::pack2(e[6], e[7])};
       }
-    if (hh == 0) LSE[qrow] = (b + __builtin_amdgcn_logf(ltot)) * kLn2;
+    lsum = lsum * hist + ls;
+    // keep P(j) and the row sum in the block of the MFMAs they overlap,
+    // instead of letting them sink past the rescale branch
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(p[kc]));
+    asm volatile("" : "+v"(lsum));
+    return hist;
+  };
+  // rare path: some row of the wave moved its base -> rescale O
+  auto rescale = [&](int j, float hist) {
+    if (DIAG && j >= 1 && hh == 0 && qrow < S && hist < 1.f) ++n_events;
+    if (j >= 1 && __builtin_amdgcn_ballot_w64(hist < 1.f) != 0) {
+#pragma unroll
+      for (int jd = 0; jd < NDB; ++jd) o[jd] *= hist;
+    }
+  };
+
+  f32x16 sA[NKB], sB[NKB];  // S(j) lives in sA for even j, sB for odd j
+  u32x4 pA[NKC], pB[NKC];   // P(j) likewise (only pA is used with two stages)
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) pB[kc] = (u32x4){};  // P(-1) = 0
+
+  // ---- prologue: K(0), K(1) (and V(0) with two stages) in LDS; S(0) --------
+  // With three stages iteration 0 runs the steady-state block with P(-1) = 0
+  // against V buffer 1, so that buffer must hold finite values (0 * NaN
+  // would poison O).
+  dma_k(lk0, 0);
+  if (ntiles > 1) dma_k(lk1, 1);
+  if constexpr (P3) {
+#pragma unroll
+    for (int i = 0; i < TL::bytes / (16 * kThreads); ++i)
+      *(__attribute__((address_space(3))) u32x4*)(lv1 + 16 * (tid + i * kThreads)) = (u32x4){};
+  } else {
+    dma_v(lv0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (nw > 0) qk(sA, lk0);
+  __syncthreads();  // ks0 is refilled with K(2) in iteration 0
+
+  // ---- iteration j (PH = j % 2). DMA first (K(j+2); V(j) with three stages,
+  // V(j+1) with two). A wave that still has tile j then runs one scheduling
+  // block: S(j+1) = QK and softmax(S(j)) -> P(j), plus P(j-1).V(j-1) with
+  // three stages; with two stages the rescale and P(j).V(j) follow. At the
+  // wave's last tile the S(j+1) it computes is not used. With three stages
+  // iteration nw only drains P(nw-1).V(nw-1). The wave keeps issuing its
+  // share of the DMA and the barriers until the work-group's last tile.
+  auto iter = [&](auto ph, int j) {
+    constexpr int PH = decltype(ph)::value;
+    f32x16(&scur)[NKB] = pick<PH>(sB, sA);
+    f32x16(&snext)[NKB] = pick<PH>(sA, sB);
+    u32x4(&pcur)[NKC] = P3 ? pick<PH>(pB, pA) : pA;
+    u32x4(&pprev)[NKC] = pick<PH>(pA, pB);
+    lds_char* k_next = PH ? lk0 : lk1;  // holds K(j+1)
+    lds_char* k_dma = PH ? lk1 : lk0;   // receives K(j+2)
+    lds_char* v_cur = PH ? lv1 : lv0;   // V(j) (two stages) / receives V(j) (three)
+    lds_char* v_oth = PH ? lv0 : lv1;   // V(j-1) (three stages) / receives V(j+1) (two)
+    if constexpr (P3) {
+      if (j < ntiles) dma_v(v_cur, j);
+    } else {
+      if (j + 1 < ntiles) dma_v(v_oth, j + 1);
+    }
+    if (j + 2 < ntiles) dma_k(k_dma, j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (j < nw) {
+      const int kv0 = j * BN;
+      if ((CAUSAL && kv0 + BN - 1 > q0w) || kv0 + BN > S) mask(scur, kv0);
+      qk(snext, k_next);
+      if constexpr (P3) pv(pprev, v_oth);
+      const float hist = softmax(scur, pcur);
+      rescale(j, hist);
+      if constexpr (!P3) pv(pcur, v_cur);
+    } else if (P3 && j == nw) {
+      pv(pprev, v_oth);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  const int niter = P3 ? ntiles + 1 : ntiles;
+  int j = 0;
+  for (; j + 1 < niter; j += 2) {
+    iter(IC<0>{}, j);
+    iter(IC<1>{}, j + 1);
+  }
+  if (j < niter) iter(IC<0>{}, j);
+
+  // ---- epilogue: normalise once, write O and lse ---------------------------
+  // Rows past S are dropped by the buffer range check.
+  const float ltot = sum_xor32(lsum);
+  if (wave_live) {
+    const float inv = 1.f / ltot;
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const f32x16& a = o[jd];
+        const int r0 = 8 * g;
+        const u32x4 w = {Ops<T>::pack2(a[r0 + 0] * inv, a[r0 + 1] * inv),
+                         Ops<T>::pack2(a[r0 + 2] * inv, a[r0 + 3] * inv),
+                         Ops<T>::pack2(a[r0 + 4] * inv, a[r0 + 5] * inv),
+                         Ops<T>::pack2(a[r0 + 6] * inv, a[r0 + 7] * inv)};
+        // accumulator element r0+e of lane (i32, hh) is d = 32jd + 16g + 8hh + e
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_frag_off<D>(qrow, jd, g, hh), 0, 0);
+      }
+    if (hh == 0) {
+      const float l2 = (b + __builtin_amdgcn_logf(ltot)) * kLn2;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l2), rl,
+                                            (uint32_t)qrow * 4u, 0, 0);
+    }
   }
   if (DIAG && n_events) atomicAdd(events, (unsigned long long)n_events);
 }
@@ -333,7 +438,7 @@ static int validate(const void* q, const void* k, const void* v, void* o, float*
     *empty = true;
     return FA_OK;
   }
-  if (S > (1 << 30)) return FA_ERR_DIM;
+  if ((long long)S * D * 2 >= (1LL << 31)) return FA_ERR_DIM;  // 32-bit buffer offsets
   const long long rows = (long long)B * H * S;
   if (rows * D > (1LL << 40)) return FA_ERR_DIM;
   if ((long long)B * H * num_q_tiles(S) >= (1LL << 31)) return FA_ERR_DIM;
@@ -400,7 +505,7 @@ int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n, int* thr
                 long long* work_groups) {
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (block_m) *block_m = fa::kBM;
-  if (block_n) *block_n = D == 64 ? fa::TileCfg<64>::BN : fa::TileCfg<128>::BN;
+  if (block_n) *block_n = fa::kBN;
   if (threads) *threads = fa::kThreads;
   if (work_groups)
     *work_groups = (B < 0 || H < 0 || S < 0) ? 0 : (long long)B * H * fa::num_q_tiles(S);

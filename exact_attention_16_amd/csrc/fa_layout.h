@@ -1,14 +1,14 @@
 // Index math of the gfx950 attention-forward kernel: work decomposition,
-// LDS layouts (with XOR swizzles), MFMA operand / accumulator lane mappings
-// and global offsets.
+// LDS tile layouts (XOR-swizzled 16-byte chunks), the DMA, MFMA-operand and
+// transposed-read lane mappings, and global offsets.
 //
 // Everything here is plain integer arithmetic usable from device code and
-// from host code (the host-side layout checker compiles this header with a
-// normal C++ compiler and enumerates every access the kernel makes).
+// from host code: the host-side layout checker compiles this header with an
+// ordinary C++ compiler and enumerates every access the kernel makes.
 //
 // Notation follows the pages: a work-group owns one block of query rows
-// ("Q tile", Br/BM rows) of one (batch, head) and streams key/value blocks
-// ("KV tiles", Bc/BN keys) past it (hotdry.top, "FlashAttention的Triton性能
+// (a "Q tile", Br rows) of one (batch, head) and streams key/value blocks
+// ("KV tiles", Bc keys) past it (hotdry.top, "FlashAttention的Triton性能
 // 考古学", sections on the v2 loop order and the (cdiv(S, Bc), B*N_h) grid).
 #pragma once
 #include <stddef.h>
@@ -27,29 +27,17 @@ constexpr int kWaves = 4;                   // waves (64 lanes) per work-group
 constexpr int kThreads = 64 * kWaves;       // 256
 constexpr int kRowsPerWave = 32;            // query rows owned by one wave
 constexpr int kBM = kRowsPerWave * kWaves;  // 128 query rows per work-group
+constexpr int kBN = 64;                     // keys per KV tile
 
-// Keys per KV tile. D=128 uses 64 keys (K and V^T tiles of 16 KiB each);
-// D=64 uses 128 keys (same 16 KiB) so that the per-tile overhead (row-max
-// exchange, rescale test, barrier) is amortised over more scores.
-template <int D> struct TileCfg;
-template <> struct TileCfg<64> { static constexpr int BN = 128; };
-template <> struct TileCfg<128> { static constexpr int BN = 64; };
-
-template <int D> struct Lds {
-  static constexpr int BN = TileCfg<D>::BN;
-  static constexpr int kRowBytes = D * 2;           // K tile row (one key)
-  static constexpr int vRowBytes = BN * 2;          // V^T tile row (one d)
-  static constexpr int kBytes = BN * D * 2;         // K tile
-  static constexpr int vBytes = BN * D * 2;         // V^T tile
-  static constexpr int stageBytes = kBytes + vBytes;
-  static constexpr int totalBytes = 2 * stageBytes; // double buffered
-  // global -> LDS staging work per thread
-  static constexpr int kChunks = BN * D / 8;        // 16-byte chunks of K
-  static constexpr int kChunksPerThread = kChunks / kThreads;
-  static constexpr int vUnits = (BN / 4) * (D / 8); // 4 keys x 8 d units of V
-  static constexpr int vUnitsPerThread = vUnits / kThreads;
-  static_assert(kChunks % kThreads == 0, "K staging must divide evenly");
-  static_assert(vUnits % kThreads == 0, "V staging must divide evenly");
+// One K or V tile in LDS: BN rows (keys) of D 16-bit elements, row-major,
+// each row split in 16-byte chunks whose order is XOR-swizzled per row.
+template <int D> struct Tile {
+  static constexpr int BN = kBN;
+  static constexpr int rowBytes = D * 2;
+  static constexpr int chunks = D / 8;                      // 16-byte chunks per row
+  static constexpr int bytes = BN * rowBytes;               // 8 KiB (D=64) / 16 KiB (D=128)
+  static constexpr int dmaPerWave = bytes / 1024 / kWaves;  // 1-KiB DMA issues per wave
+  static_assert(bytes % (1024 * kWaves) == 0, "tile must split into whole DMA issues");
 };
 
 // ------------------------------------------------------- work decomposition
@@ -79,33 +67,66 @@ FA_HD int wave_kv_end(int q0w, int S, bool causal) {
   return e < S ? e : S;
 }
 
-// ------------------------------------------------------------- LDS swizzle
-// Byte offset of 16-byte chunk c of row r, in a buffer of rows of row_bytes
-// (128 or 256). The chunk index is XOR-ed with a function g of the row bits
-// b0..b5, chosen for the kernel's access patterns:
-//  * operand reads: a wave reads rows 32*blk + row_perm32(lane%32) at one
-//    chunk; 16 lanes (one 64-bank cycle) cover rows with b0..b3 free, 8
-//    lanes (one 32-bank cycle) rows with b0, b1, b3 free -> g is a bijection
-//    of those bits, so reads are conflict-free under either bank model;
-//  * V^T staging writes: rows 8*dc + dd with dc (bits b3..b5) varying across
-//    lanes -> g also varies with b3..b5 (writes at most 2-way).
-// 256-byte rows (16 chunks): g = (b0^b3, b1^b4, b3^b5, b2^b4^b5).
-// 128-byte rows (8 chunks, 2 rows per 256-byte line): g = (b0^b1^b5,
-// b0^b2^b4, b3).
-FA_HD int swz_g256(int r) {
-  const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
-  const int b4 = (r >> 4) & 1, b5 = (r >> 5) & 1;
-  return (b0 ^ b3) | ((b1 ^ b4) << 1) | ((b3 ^ b5) << 2) | ((b2 ^ b4 ^ b5) << 3);
+// --------------------------------------------------------- LDS swizzles
+// Byte offset of logical 16-byte chunk c of row r = r*rowBytes + (c ^ g(r))*16.
+//
+// K tile (rows = keys): the S^T MFMA operand read has 16 lanes of one
+// 64-bank cycle read rows {0..15} (+ a multiple of 16) at one chunk, and 8
+// lanes of one 32-bank cycle rows {0..3, 8..11}; g is a bijection of the
+// row bits those lanes vary, so either bank model sees no conflict.
+//   D=128 (256-byte rows): g = row bits (b0, b1, b3, b2)  [swap of b2, b3]
+//   D=64  (128-byte rows, two per 256 bytes): g = (b0^b1, b0^b2, b3)
+template <int D> FA_HD int gk(int r);
+template <> FA_HD int gk<128>(int r) { return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1); }
+template <> FA_HD int gk<64>(int r) {
+  return ((r ^ (r >> 1)) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
-FA_HD int swz_g128(int r) {
-  const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
-  const int b4 = (r >> 4) & 1, b5 = (r >> 5) & 1;
-  return (b0 ^ b1 ^ b5) | ((b0 ^ b2 ^ b4) << 1) | (b3 << 2);
+// V tile (rows = keys): the transposed read has the 32 lanes of one cycle
+// read 4 consecutive rows x 64 bytes; g moves each of the 4 rows to its own
+// 64-byte quarter of the bank space.
+//   D=128: g = 4*(r mod 4);  D=64: g = 4*((r/2) mod 2)
+template <int D> FA_HD int gv(int r);
+template <> FA_HD int gv<128>(int r) { return 4 * (r & 3); }
+template <> FA_HD int gv<64>(int r) { return 4 * ((r >> 1) & 1); }
+
+template <int D> FA_HD uint32_t k_off(int r, int c) {
+  return (uint32_t)(r * Tile<D>::rowBytes + ((c ^ gk<D>(r)) << 4));
 }
-FA_HD uint32_t swz(int r, int c, int row_bytes) {
-  return row_bytes == 256 ? (uint32_t)(r * 256 + ((c ^ swz_g256(r)) << 4))
-                          : (uint32_t)(r * 128 + ((c ^ swz_g128(r)) << 4));
+template <int D> FA_HD uint32_t v_off(int r, int c) {
+  return (uint32_t)(r * Tile<D>::rowBytes + ((c ^ gv<D>(r)) << 4));
 }
+
+// ------------------------------------------------ global -> LDS DMA (16 B)
+// A buffer load with the LDS bit writes lane p's 16 bytes to LDS base + 16*p,
+// so each DMA issue fills one 1-KiB block of the tile. Lane p fetches the
+// logical chunk that belongs at its LDS slot; dma_src_* return that chunk's
+// byte offset within the (contiguous) global tile.
+// K: issue i of wave w fills block i*kWaves + w, so successive issues are 16
+// rows apart (D=128; 32 rows for D=64) and gk, which reads row bits 0..3,
+// repeats: the source offset of issue i is issue 0's plus i*4096 bytes.
+// V: issue i of wave w fills block w*dmaPerWave + i; gv reads row bits 0..1
+// only, so issue i is issue 0's plus i*1024 bytes.
+template <int D> FA_HD int dma_block_k(int w, int i) { return i * kWaves + w; }
+template <int D> FA_HD int dma_block_v(int w, int i) { return w * Tile<D>::dmaPerWave + i; }
+template <int D> FA_HD void dma_slot(int block, int lane, int* r, int* pc) {
+  const int idx = block * 64 + lane;
+  *r = idx / Tile<D>::chunks;
+  *pc = idx % Tile<D>::chunks;
+}
+template <int D> FA_HD uint32_t dma_src_k(int w, int i, int lane) {
+  int r, pc;
+  dma_slot<D>(dma_block_k<D>(w, i), lane, &r, &pc);
+  return (uint32_t)(r * Tile<D>::rowBytes + ((pc ^ gk<D>(r)) << 4));
+}
+template <int D> FA_HD uint32_t dma_src_v(int w, int i, int lane) {
+  int r, pc;
+  dma_slot<D>(dma_block_v<D>(w, i), lane, &r, &pc);
+  return (uint32_t)(r * Tile<D>::rowBytes + ((pc ^ gv<D>(r)) << 4));
+}
+template <int D> FA_HD uint32_t dma_lds_k(int w, int i) { return (uint32_t)dma_block_k<D>(w, i) * 1024u; }
+template <int D> FA_HD uint32_t dma_lds_v(int w, int i) { return (uint32_t)dma_block_v<D>(w, i) * 1024u; }
+constexpr uint32_t kDmaStrideK = 4096;  // source offset step per K issue
+constexpr uint32_t kDmaStrideV = 1024;  // source offset step per V issue
 
 // ------------------------------------------------ MFMA lane mappings (32x32)
 // v_mfma_f32_32x32x16_{f16,bf16}: operand A row i / operand B column j is
@@ -114,80 +135,53 @@ FA_HD uint32_t swz(int r, int c, int row_bytes) {
 // column l%32).
 //
 // The kernel computes S^T = K Q^T (rows = keys, columns = query rows) so that
-// a lane ends up owning one query row, and loads K rows in the order
-// row_perm32 (swap of bits 2 and 3) so that accumulator elements 0..7 of a
-// lane are 8 consecutive keys and 8..15 the next 8 of its k-half. Those 8
-// consecutive keys are exactly the k-run the P.V MFMA needs from that lane,
-// so P goes from the S accumulator to the P.V operand without leaving the
-// lane.
+// a lane owns one query row, and feeds K rows in the order row_perm32 (swap
+// of bits 2 and 3) so that accumulator elements 0..7 of a lane are 8
+// consecutive keys and 8..15 the next 8 of its k-half. Those 8 consecutive
+// keys are exactly the k-run the P.V MFMA needs from that lane, so P goes
+// from the S accumulator to the P.V operand without leaving the lane.
 FA_HD int row_perm32(int r) { return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // Key (within a 32-key block) held in accumulator element r by k-half hh.
 FA_HD int acc_key32(int r, int hh) { return 16 * (r >> 3) + 8 * hh + (r & 7); }
 
-// ---------------------------------------------- LDS offsets used by the kernel
-// K tile: row = key (0..BN-1), 8-element chunk ch (0..D/8-1).
-template <int D> FA_HD uint32_t k_lds(int key, int ch) { return swz(key, ch, Lds<D>::kRowBytes); }
-// V^T tile: row = d (0..D-1), 8-key chunk kc8 (0..BN/8-1); byte offset within
-// the chunk for 4-key quarter q4 (0 or 1) is 8*q4.
-template <int D> FA_HD uint32_t vt_lds(int d, int kc8) {
-  return (uint32_t)Lds<D>::kBytes + swz(d, kc8, Lds<D>::vRowBytes);
-}
-
-// K staging: chunk index idx -> (key, ch); consecutive threads take
-// consecutive 16-byte chunks of the contiguous K tile (coalesced).
-template <int D> FA_HD void k_stage_map(int idx, int* key, int* ch) {
-  *key = idx / (D / 8);
-  *ch = idx % (D / 8);
-}
-// V staging: unit u -> (kg, dc): keys 4*kg..4*kg+3, d = 8*dc..8*dc+7;
-// consecutive threads take consecutive d-chunks of the same 4 rows.
-template <int D> FA_HD void v_stage_map(int u, int* kg, int* dc) {
-  *kg = u / (D / 8);
-  *dc = u % (D / 8);
-}
-
-// LDS byte offsets of the kernel's accesses, per lane (lane = 0..63):
-// S^T MFMA operand A: K row 32*kb + row_perm32(lane%32), d-chunk 2*j + lane/32.
+// S^T operand A of contraction step j (d = 16j..16j+15) for 32-key block kb:
+// lane reads K row 32*kb + row_perm32(lane%32), chunk 2j + lane/32.
+// gk depends only on row bits 0..3, so kb adds exactly kb*32*rowBytes; and
+// (2j + hh) ^ g = 2(j ^ g/2) + ((hh ^ g) & 1) with the row base a multiple
+// of 128, so step j's offset is step 0's XOR (j << 5).
 template <int D> FA_HD uint32_t k_read_off(int kb, int j, int lane) {
-  return k_lds<D>(32 * kb + row_perm32(lane & 31), 2 * j + (lane >> 5));
-}
-// O^T MFMA operand A: V^T row 32*jd + row_perm32(lane%32), keys 16*kc + 8*(lane/32) + 0..7.
-template <int D> FA_HD uint32_t vt_read_off(int jd, int kc, int lane) {
-  return vt_lds<D>(32 * jd + row_perm32(lane & 31), 2 * kc + (lane >> 5));
-}
-// K staging store of chunk idx.
-template <int D> FA_HD uint32_t k_write_off(int idx) {
-  int key, ch;
-  k_stage_map<D>(idx, &key, &ch);
-  return k_lds<D>(key, ch);
-}
-// V^T staging store of unit u, row 8*dc + dd: keys 4*kg..4*kg+3 as 8 bytes.
-// V[key][d] lands at vt_lds(d, key/8) + 2*(key%8).
-template <int D> FA_HD uint32_t vt_write_off(int u, int dd) {
-  int kg, dc;
-  v_stage_map<D>(u, &kg, &dc);
-  return vt_lds<D>(8 * dc + dd, kg >> 1) + 8 * (kg & 1);
+  return k_off<D>(32 * kb + row_perm32(lane & 31), 2 * j + (lane >> 5));
 }
 
-// ------------------------------------------ global element offsets (per head)
-// Q operand fragment j of a lane: row qrow (clamped), d = 16*j + 8*hh + 0..7.
-template <int D> FA_HD size_t q_frag_off(int qrow_c, int j, int hh) {
-  return (size_t)qrow_c * D + 16 * j + 8 * hh;
+// O^T operand A (V^T) of d-block jd and 16-key chunk kc, read with
+// ds_read_b64_tr_b16 in two halves rd = 0, 1 (keys 16kc + 8h + 4rd + 0..3).
+// The instruction works on groups of 16 lanes: source lane s of a group
+// reads 4 consecutive 16-bit elements, and result lane i receives element
+// i%4 of source lanes i/4, i/4+4, i/4+8, i/4+12. Source lane s = 4e + q of
+// group (h = lane/32, g2 = lane/16 % 2) reads key row 16kc + 8h + 4rd + e at
+// d = 32jd + 16g2 + 8(q%2) + 4(q/2) .. +3, so result lane i = 4q' + c' holds
+// V[16kc + 8h + 4rd + e][32jd + row_perm32(16g2 + i)] for e = 0..3: the
+// MFMA row of lane l is d = 32jd + row_perm32(l%32) with keys 8h + 4rd + e.
+// gv depends only on row bits 0..1, so kc and rd add kc*16*rowBytes and
+// rd*4*rowBytes; gv only flips chunk bits 2..3, where jd sits, so block jd's
+// offset is block 0's XOR (jd << 6).
+template <int D> FA_HD uint32_t v_tr_off(int jd, int kc, int rd, int lane) {
+  const int i = lane & 15, g2 = (lane >> 4) & 1, h = lane >> 5;
+  const int row = 16 * kc + 8 * h + 4 * rd + (i >> 2);
+  const int c = 4 * jd + 2 * g2 + (i & 1);
+  return v_off<D>(row, c) + 8 * ((i >> 1) & 1);
 }
-// 8-element chunk ch of global row `row` of K or V.
-template <int D> FA_HD size_t kv_chunk_off(int row, int ch) { return (size_t)row * D + 8 * ch; }
+
+// ------------------------------------------ global byte offsets (per head)
+// Q operand fragment j of a lane: row qrow, d = 16*j + 8*hh + 0..7.
+template <int D> FA_HD uint32_t q_frag_off(int qrow, int j, int hh) {
+  return (uint32_t)(qrow * Tile<D>::rowBytes + (16 * j + 8 * hh) * 2);
+}
 // O store of a lane: row qrow, d = 32*jd + 16*g + 8*hh + 0..7 (accumulator
 // elements 8*g .. 8*g+7 of d-block jd).
-template <int D> FA_HD size_t o_frag_off(int qrow, int jd, int g, int hh) {
-  return (size_t)qrow * D + 32 * jd + 16 * g + 8 * hh;
-}
-
-// Global row of key `key` of the tile starting at kv0, clamped into [0, S).
-// Rows past the end are masked before use, so any in-range row will do.
-FA_HD int kv_row(int kv0, int key, int S) {
-  const int r = kv0 + key;
-  return r < S ? r : S - 1;
+template <int D> FA_HD uint32_t o_frag_off(int qrow, int jd, int g, int hh) {
+  return (uint32_t)(qrow * Tile<D>::rowBytes + (32 * jd + 16 * g + 8 * hh) * 2);
 }
 
 }  // namespace fa

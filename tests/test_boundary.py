@@ -40,6 +40,17 @@ def test_library_exports_every_declared_symbol():
         assert exported == _declared()
 
 
+def test_kernel_launch_stubs_are_defined():
+    """Every kernel instantiation the launcher references has a host stub."""
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("no nm")
+    out = subprocess.run([nm, "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    stubs = [l for l in out.splitlines() if "device_stub" in l]
+    assert len(stubs) == 24
+    assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
+
+
 def test_version_and_strerror():
     assert fa.fa_version() == 100
     for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG):
@@ -49,7 +60,7 @@ def test_version_and_strerror():
 
 def test_tile_query():
     assert fa.fa_fwd_tile(128, 2, 16, 8192) == (128, 64, 256, 2 * 16 * 64)
-    assert fa.fa_fwd_tile(64, 10, 64, 1024) == (128, 128, 256, 640 * 8)
+    assert fa.fa_fwd_tile(64, 10, 64, 1024) == (128, 64, 256, 640 * 8)
     assert fa.fa_fwd_tile(64, 1, 1, 129)[3] == 2
     with pytest.raises(fa.FaError):
         fa.fa_fwd_tile(96)
