@@ -20,6 +20,11 @@ LIB_PATH = os.path.join(HERE, "libfa_fwd.so")
 FA_F16 = 0
 FA_BF16 = 1
 
+# kernel choice of fa_fwd_diag
+VARIANT_AUTO = 0
+VARIANT_FOUR_WAVE = 1
+VARIANT_PING_PONG = 2
+
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_DIM", -3: "FA_ERR_UNSUPPORTED",
     -4: "FA_ERR_ALIGN", -5: "FA_ERR_SCALE", -6: "FA_ERR_ALIAS", -7: "FA_ERR_HIP",
@@ -35,7 +40,7 @@ SIGNATURES = {
     "fa_fwd": (_I, _FWD_ARGS + [_I]),
     "fa_fwd_f16": (_I, _FWD_ARGS),
     "fa_fwd_bf16": (_I, _FWD_ARGS),
-    "fa_fwd_diag": (_I, _FWD_ARGS + [_I, _I, _P]),
+    "fa_fwd_diag": (_I, _FWD_ARGS + [_I, _I, _I, _P]),
     "fa_fwd_tile": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
                          ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_longlong)]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
@@ -91,9 +96,9 @@ def fa_fwd_bf16(q, k, v, o, lse, B, H, S, D, causal, scale, stream, check=True):
 
 
 def fa_fwd_diag(q, k, v, o, lse, B, H, S, D, causal, scale, stream, dtype,
-                threshold_log2, rescale_events, check=True):
+                threshold_log2, variant, rescale_events, check=True):
     st = load().fa_fwd_diag(q, k, v, o, lse, B, H, S, D, int(causal), scale, stream,
-                            dtype, threshold_log2, rescale_events)
+                            dtype, threshold_log2, variant, rescale_events)
     return _check(st, "fa_fwd_diag") if check else st
 
 

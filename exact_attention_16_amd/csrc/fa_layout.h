@@ -1,10 +1,10 @@
-// Index math of the gfx950 attention-forward kernel: work decomposition,
+// Index math of the gfx950 attention-forward kernels: work decomposition,
 // LDS tile layouts (XOR-swizzled 16-byte chunks), the DMA, MFMA-operand and
 // transposed-read lane mappings, and global offsets.
 //
 // Everything here is plain integer arithmetic usable from device code and
 // from host code: the host-side layout checker compiles this header with an
-// ordinary C++ compiler and enumerates every access the kernel makes.
+// ordinary C++ compiler and enumerates every access the kernels make.
 //
 // Notation follows the pages: a work-group owns one block of query rows
 // (a "Q tile", Br rows) of one (batch, head) and streams key/value blocks
@@ -22,42 +22,64 @@
 
 namespace fa {
 
-// ---------------------------------------------------------------- tile sizes
-constexpr int kWaves = 4;                   // waves (64 lanes) per work-group
-constexpr int kThreads = 64 * kWaves;       // 256
-constexpr int kRowsPerWave = 32;            // query rows owned by one wave
-constexpr int kBM = kRowsPerWave * kWaves;  // 128 query rows per work-group
-constexpr int kBN = 64;                     // keys per KV tile
+constexpr int kRowsPerWave = 32;  // query rows owned by one wave (one MFMA column block)
 
-// One K or V tile in LDS: BN rows (keys) of D 16-bit elements, row-major,
-// each row split in 16-byte chunks whose order is XOR-swizzled per row.
-template <int D> struct Tile {
-  static constexpr int BN = kBN;
+// A kernel configuration: head dimension D, NW waves (64 lanes) per
+// work-group, BN keys per KV tile. One K or V tile in LDS holds BN rows
+// (keys) of D 16-bit elements, row-major, each row split in 16-byte chunks
+// whose order is XOR-swizzled per row.
+template <int D_, int NW_, int BN_> struct Cfg {
+  static constexpr int D = D_;
+  static constexpr int NW = NW_;
+  static constexpr int BN = BN_;
+  static constexpr int threads = 64 * NW;
+  static constexpr int BM = kRowsPerWave * NW;           // query rows per work-group
   static constexpr int rowBytes = D * 2;
-  static constexpr int chunks = D / 8;                      // 16-byte chunks per row
-  static constexpr int bytes = BN * rowBytes;               // 8 KiB (D=64) / 16 KiB (D=128)
-  static constexpr int dmaPerWave = bytes / 1024 / kWaves;  // 1-KiB DMA issues per wave
-  static_assert(bytes % (1024 * kWaves) == 0, "tile must split into whole DMA issues");
+  static constexpr int chunks = D / 8;                   // 16-byte chunks per row
+  static constexpr int tileBytes = BN * rowBytes;        // one K or V tile
+  static constexpr int dmaPerWave = tileBytes / 1024 / NW;  // 1-KiB DMA issues per wave
+  static constexpr uint32_t dmaStrideK = NW * 1024u;     // source step per K issue
+  static constexpr uint32_t dmaStrideV = 1024u;          // source step per V issue
+  static_assert(tileBytes % (1024 * NW) == 0, "tile must split into whole DMA issues");
+  static_assert(BN % 32 == 0, "KV tile must be whole 32-key MFMA blocks");
 };
+
+// The two kernels: four waves (128 query rows) with a two- or three-stage
+// register pipeline per wave, for grids too small to fill the chip with
+// 256-row tiles; eight waves (256 rows) in two groups that alternate MFMA
+// and softmax phases (ping-pong) otherwise. The ping-pong kernel uses 128-key
+// tiles at D=64 so that an MFMA phase (32 MFMAs) balances a softmax phase.
+template <int D> using Cfg4 = Cfg<D, 4, 64>;
+template <int D> using Cfg8 = Cfg<D, 8, (D == 64 ? 128 : 64)>;
 
 // ------------------------------------------------------- work decomposition
 // One work-group per (Q tile, batch*head). Under a causal mask Q tile t needs
 // keys [0, (t+1)*BM), so work grows with t; tiles are issued heaviest first
 // (longest-processing-time order) so that the short ones fill the tail.
-// Consecutive work-group ids take consecutive heads, so with B*H a multiple
-// of 8 every Q tile of a head lands on the same XCD (ids are dealt to the 8
-// XCDs round-robin) and its K/V stay in that XCD's L2.
+// Work-group ids are dealt to the 8 XCDs round-robin (XCD = id mod 8), each
+// XCD with its own L2. When B*H is a multiple of 8, XCD x takes heads x,
+// x+8, x+16, ... one head at a time: all Q tiles of a head run together on
+// one XCD, sweeping that head's K/V through one L2. Otherwise ids go to
+// heads in turn, Q tile order outermost.
 FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh) {
-  const int ord = bid / BH;
-  *bh = bid - ord * BH;
+  int ord;
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, k = bid >> 3;  // XCD, and this id's rank on it
+    const int lh = k / nqt;               // local head on the XCD
+    ord = k - lh * nqt;
+    *bh = x + 8 * lh;
+  } else {
+    ord = bid / BH;
+    *bh = bid - ord * BH;
+  }
   *qt = causal ? (nqt - 1 - ord) : ord;
 }
 
-FA_HD int num_q_tiles(int S) { return (S + kBM - 1) / kBM; }
+FA_HD int num_q_tiles(int S, int BM) { return (S + BM - 1) / BM; }
 
 // Exclusive upper bound of the keys a work-group's Q tile can see.
-FA_HD int tile_kv_end(int qt, int S, bool causal) {
-  const int e = causal ? (qt + 1) * kBM : S;
+FA_HD int tile_kv_end(int qt, int S, bool causal, int BM) {
+  const int e = causal ? (qt + 1) * BM : S;
   return e < S ? e : S;
 }
 
@@ -90,10 +112,10 @@ template <> FA_HD int gv<128>(int r) { return 4 * (r & 3); }
 template <> FA_HD int gv<64>(int r) { return 4 * ((r >> 1) & 1); }
 
 template <int D> FA_HD uint32_t k_off(int r, int c) {
-  return (uint32_t)(r * Tile<D>::rowBytes + ((c ^ gk<D>(r)) << 4));
+  return (uint32_t)(r * D * 2 + ((c ^ gk<D>(r)) << 4));
 }
 template <int D> FA_HD uint32_t v_off(int r, int c) {
-  return (uint32_t)(r * Tile<D>::rowBytes + ((c ^ gv<D>(r)) << 4));
+  return (uint32_t)(r * D * 2 + ((c ^ gv<D>(r)) << 4));
 }
 
 // ------------------------------------------------ global -> LDS DMA (16 B)
@@ -101,32 +123,30 @@ template <int D> FA_HD uint32_t v_off(int r, int c) {
 // so each DMA issue fills one 1-KiB block of the tile. Lane p fetches the
 // logical chunk that belongs at its LDS slot; dma_src_* return that chunk's
 // byte offset within the (contiguous) global tile.
-// K: issue i of wave w fills block i*kWaves + w, so successive issues are 16
-// rows apart (D=128; 32 rows for D=64) and gk, which reads row bits 0..3,
-// repeats: the source offset of issue i is issue 0's plus i*4096 bytes.
+// K: issue i of wave w fills block i*NW + w, so successive issues are NW
+// blocks (a multiple of 16 rows) apart and gk, which reads row bits 0..3,
+// repeats: the source offset of issue i is issue 0's plus i*NW*1024 bytes.
 // V: issue i of wave w fills block w*dmaPerWave + i; gv reads row bits 0..1
 // only, so issue i is issue 0's plus i*1024 bytes.
-template <int D> FA_HD int dma_block_k(int w, int i) { return i * kWaves + w; }
-template <int D> FA_HD int dma_block_v(int w, int i) { return w * Tile<D>::dmaPerWave + i; }
-template <int D> FA_HD void dma_slot(int block, int lane, int* r, int* pc) {
+template <class C> FA_HD int dma_block_k(int w, int i) { return i * C::NW + w; }
+template <class C> FA_HD int dma_block_v(int w, int i) { return w * C::dmaPerWave + i; }
+template <class C> FA_HD void dma_slot(int block, int lane, int* r, int* pc) {
   const int idx = block * 64 + lane;
-  *r = idx / Tile<D>::chunks;
-  *pc = idx % Tile<D>::chunks;
+  *r = idx / C::chunks;
+  *pc = idx % C::chunks;
 }
-template <int D> FA_HD uint32_t dma_src_k(int w, int i, int lane) {
+template <class C> FA_HD uint32_t dma_src_k(int w, int i, int lane) {
   int r, pc;
-  dma_slot<D>(dma_block_k<D>(w, i), lane, &r, &pc);
-  return (uint32_t)(r * Tile<D>::rowBytes + ((pc ^ gk<D>(r)) << 4));
+  dma_slot<C>(dma_block_k<C>(w, i), lane, &r, &pc);
+  return (uint32_t)(r * C::rowBytes + ((pc ^ gk<C::D>(r)) << 4));
 }
-template <int D> FA_HD uint32_t dma_src_v(int w, int i, int lane) {
+template <class C> FA_HD uint32_t dma_src_v(int w, int i, int lane) {
   int r, pc;
-  dma_slot<D>(dma_block_v<D>(w, i), lane, &r, &pc);
-  return (uint32_t)(r * Tile<D>::rowBytes + ((pc ^ gv<D>(r)) << 4));
+  dma_slot<C>(dma_block_v<C>(w, i), lane, &r, &pc);
+  return (uint32_t)(r * C::rowBytes + ((pc ^ gv<C::D>(r)) << 4));
 }
-template <int D> FA_HD uint32_t dma_lds_k(int w, int i) { return (uint32_t)dma_block_k<D>(w, i) * 1024u; }
-template <int D> FA_HD uint32_t dma_lds_v(int w, int i) { return (uint32_t)dma_block_v<D>(w, i) * 1024u; }
-constexpr uint32_t kDmaStrideK = 4096;  // source offset step per K issue
-constexpr uint32_t kDmaStrideV = 1024;  // source offset step per V issue
+template <class C> FA_HD uint32_t dma_lds_k(int w, int i) { return (uint32_t)dma_block_k<C>(w, i) * 1024u; }
+template <class C> FA_HD uint32_t dma_lds_v(int w, int i) { return (uint32_t)dma_block_v<C>(w, i) * 1024u; }
 
 // ------------------------------------------------ MFMA lane mappings (32x32)
 // v_mfma_f32_32x32x16_{f16,bf16}: operand A row i / operand B column j is
@@ -134,9 +154,9 @@ constexpr uint32_t kDmaStrideV = 1024;  // source offset step per V issue
 // accumulator element r of lane l is (row 8*(r/4) + 4*(l/32) + r%4,
 // column l%32).
 //
-// The kernel computes S^T = K Q^T (rows = keys, columns = query rows) so that
-// a lane owns one query row, and feeds K rows in the order row_perm32 (swap
-// of bits 2 and 3) so that accumulator elements 0..7 of a lane are 8
+// The kernels compute S^T = K Q^T (rows = keys, columns = query rows) so
+// that a lane owns one query row, and feed K rows in the order row_perm32
+// (swap of bits 2 and 3) so that accumulator elements 0..7 of a lane are 8
 // consecutive keys and 8..15 the next 8 of its k-half. Those 8 consecutive
 // keys are exactly the k-run the P.V MFMA needs from that lane, so P goes
 // from the S accumulator to the P.V operand without leaving the lane.
@@ -176,12 +196,27 @@ template <int D> FA_HD uint32_t v_tr_off(int jd, int kc, int rd, int lane) {
 // ------------------------------------------ global byte offsets (per head)
 // Q operand fragment j of a lane: row qrow, d = 16*j + 8*hh + 0..7.
 template <int D> FA_HD uint32_t q_frag_off(int qrow, int j, int hh) {
-  return (uint32_t)(qrow * Tile<D>::rowBytes + (16 * j + 8 * hh) * 2);
+  return (uint32_t)(qrow * D * 2 + (16 * j + 8 * hh) * 2);
 }
 // O store of a lane: row qrow, d = 32*jd + 16*g + 8*hh + 0..7 (accumulator
 // elements 8*g .. 8*g+7 of d-block jd).
 template <int D> FA_HD uint32_t o_frag_off(int qrow, int jd, int g, int hh) {
-  return (uint32_t)(qrow * Tile<D>::rowBytes + (32 * jd + 16 * g + 8 * hh) * 2);
+  return (uint32_t)(qrow * D * 2 + (32 * jd + 16 * g + 8 * hh) * 2);
 }
+
+// ------------------------------------- ping-pong schedule (eight waves)
+// Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs one each (wave
+// w and w+4 land on the same SIMD). Time is divided in slots separated by
+// work-group barriers; slot t of a wave runs its local phase t - group:
+// even phase 2j = MFMA phase (O += P(j-1) V(j-1), S(j) = K(j) Q^T), odd
+// phase 2j+1 = softmax phase of S(j). So in every slot one wave of each SIMD
+// multiplies while the other exponentiates. KV tile t lives in LDS stage
+// t mod kStages for both K and V. In even slot 2i each wave issues its share
+// of K(i+2) and V(i+1); at the end of odd slot 2i+1 it waits for all but its
+// latest share, so everything issued by slot 2i-2 has landed -- K(j) before
+// slot 2j, V(j) before slot 2j+2. A stage is refilled only after both groups
+// have read it: K(j-3) is last read in slot 2j-5, V(j-3) in slot 2j-3.
+constexpr int kStages = 3;
+FA_HD int pp_slots(int ntiles) { return 2 * ntiles + 2; }
 
 }  // namespace fa

@@ -70,7 +70,8 @@ typedef enum {
  *   lse      device, [B,H,S] float, 16-byte aligned, written
  *   B, H, S  >= 0; B*H*S == 0 is a no-op returning FA_OK (pointers unused).
  *            Any S >= 1 is accepted (a ragged last tile is masked).
- *            Limits: S <= 2^30, B*H*S*D <= 2^40, B*H*ceil(S/128) < 2^31.
+ *            Limits: S*D*2 < 2^31 (one head's K/V/O addressed with 32-bit
+ *            offsets), B*H*S*D <= 2^40, B*H*ceil(S/128) < 2^31.
  *   D        head dimension, 64 or 128
  *   causal   0 = every key visible; 1 = key j visible to row i iff j <= i
  *   scale    multiplier of q.k; finite and > 0 (typically 1/sqrt(D)).
@@ -106,18 +107,28 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse
  *                    by the caller; the kernel atomically adds the number
  *                    of (query row, KV tile) pairs whose running max moved
  *                    after the row's first tile. Not cleared by the library.
- * It runs a separate, instrumented instantiation of the same kernel.
+ *   variant          which kernel runs: 0 = the one fa_fwd picks for this
+ *                    shape, 1 = the four-wave kernel (128 query rows per
+ *                    work-group), 2 = the eight-wave ping-pong kernel (256
+ *                    rows). Every variant computes the same result, to
+ *                    rounding; the choice only affects speed.
+ * It runs separate, instrumented instantiations of the same kernels.
+ * Invalid threshold_log2 or variant: FA_ERR_ARG; NULL rescale_events:
+ * FA_ERR_NULL; rescale_events not 8-byte aligned: FA_ERR_ALIGN.
  */
 int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int S, int D, int causal, float scale,
-                hipStream_t stream, int dtype, int threshold_log2,
+                hipStream_t stream, int dtype, int threshold_log2, int variant,
                 unsigned long long* rescale_events);
 
 /*
- * fa_fwd_tile -- the tile shape used for head dimension D: query rows per
- * work-group, keys per KV tile, threads per work-group, and the number of
- * work-groups a call with (B, H, S) launches. Any output pointer may be
- * NULL. Returns FA_ERR_UNSUPPORTED for D not in {64, 128}.
+ * fa_fwd_tile -- the tile shape fa_fwd uses for a call with (B, H, S) at
+ * head dimension D: query rows per work-group, keys per KV tile, threads per
+ * work-group, and the number of work-groups launched. fa_fwd runs the
+ * eight-wave kernel (256 rows; 64 keys per tile at D=128, 128 at D=64) when
+ * B*H*ceil(S/256) >= 256, else the four-wave kernel (128 rows, 64 keys).
+ * Any output pointer may be NULL. Returns FA_ERR_UNSUPPORTED for D not in
+ * {64, 128}.
  */
 int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n,
                 int* threads, long long* work_groups);

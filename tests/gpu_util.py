@@ -26,10 +26,24 @@ def to_dev(bits: np.ndarray, dtype: str) -> torch.Tensor:
     return t.view(TORCH_DT[dtype]).to(device())
 
 
-def run(qb, kb, vb, dtype, causal, scale, stream=None):
-    """fa_fwd on the seeded bits; returns device tensors (o, lse)."""
+def run(qb, kb, vb, dtype, causal, scale, stream=None, variant=None):
+    """fa_fwd on the seeded bits; returns device tensors (o, lse).
+
+    variant None: fa_fwd (the kernel it picks for the shape). Otherwise
+    fa_fwd_diag with that kernel choice (fa.VARIANT_*), production threshold.
+    """
     q, k, v = (to_dev(x, dtype) for x in (qb, kb, vb))
-    o, lse = fa.attention(q, k, v, causal, scale, stream=stream)
+    if variant is None:
+        o, lse = fa.attention(q, k, v, causal, scale, stream=stream)
+    else:
+        assert stream is None
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device())
+        ev = torch.zeros(1, dtype=torch.int64, device=device())
+        B, H, S, D = q.shape
+        fa.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, S, D, int(causal), scale, torch.cuda.current_stream().cuda_stream,
+                       W.DTYPE_CODE[dtype], 8, variant, ev.data_ptr())
     torch.cuda.synchronize()
     return o, lse
 

@@ -18,7 +18,13 @@
 //  * the work decomposition visits each (Q tile, head) once, every key a row
 //    can see lies in a tile its wave computes, and O is written exactly once;
 //  * the worst LDS bank-conflict degree of every pattern, under a 64-bank
-//    model (256 bytes per cycle) and a 32-bank model (128 bytes per cycle).
+//    model (256 bytes per cycle) and a 32-bank model (128 bytes per cycle);
+//  * the eight-wave ping-pong schedule: replaying both wave groups' slots
+//    (DMA issues, waits for all but the latest pair, LDS reads) in the order
+//    the kernel code runs them, every read of a stage finds the tile it
+//    expects, landed and published by a barrier, and no DMA overwrites a
+//    stage that a wave of either group still has to read.
+// All of it for both kernel configurations (four and eight waves).
 //
 // Prints a summary and "OK"; exits non-zero on any error.
 #include <algorithm>
@@ -65,25 +71,25 @@ static int conflict_degree(const std::vector<uint32_t>& addr, int bytes, int ban
 static long tag_of(int row, int d, int D) { return (long)row * D + d; }
 
 // Simulate the DMA of one tile; returns per-byte-pair tags (one per element).
-template <int D>
+template <class C>
 static std::vector<long> dma_tile(bool is_k, int* worst64) {
-  using TL = Tile<D>;
-  std::vector<long> tag(TL::bytes / 2, -1);
+  constexpr int D = C::D;
+  std::vector<long> tag(C::tileBytes / 2, -1);
   *worst64 = 1;
-  for (int w = 0; w < kWaves; ++w)
-    for (int i = 0; i < TL::dmaPerWave; ++i) {
+  for (int w = 0; w < C::NW; ++w)
+    for (int i = 0; i < C::dmaPerWave; ++i) {
       std::vector<uint32_t> addr(64);
       for (int p = 0; p < 64; ++p) {
-        const uint32_t dst = (is_k ? dma_lds_k<D>(w, i) : dma_lds_v<D>(w, i)) + 16 * p;
-        const uint32_t src = is_k ? dma_src_k<D>(w, i, p) : dma_src_v<D>(w, i, p);
+        const uint32_t dst = (is_k ? dma_lds_k<C>(w, i) : dma_lds_v<C>(w, i)) + 16 * p;
+        const uint32_t src = is_k ? dma_src_k<C>(w, i, p) : dma_src_v<C>(w, i, p);
         // the kernel forms issue i's source offset as issue 0's plus a stride
-        CHECK(src == (is_k ? dma_src_k<D>(w, 0, p) + i * kDmaStrideK
-                           : dma_src_v<D>(w, 0, p) + i * kDmaStrideV),
+        CHECK(src == (is_k ? dma_src_k<C>(w, 0, p) + i * C::dmaStrideK
+                           : dma_src_v<C>(w, 0, p) + i * C::dmaStrideV),
               "DMA source stride w=%d i=%d p=%d", w, i, p);
         addr[p] = dst;
-        CHECK(dst % 16 == 0 && dst + 16 <= (uint32_t)TL::bytes, "DMA dst %u", dst);
-        CHECK(src % 16 == 0 && src + 16 <= (uint32_t)TL::bytes, "DMA src %u", src);
-        const int row = src / TL::rowBytes, d0 = (src % TL::rowBytes) / 2;
+        CHECK(dst % 16 == 0 && dst + 16 <= (uint32_t)C::tileBytes, "DMA dst %u", dst);
+        CHECK(src % 16 == 0 && src + 16 <= (uint32_t)C::tileBytes, "DMA src %u", src);
+        const int row = src / C::rowBytes, d0 = (src % C::rowBytes) / 2;
         // the slot must be where the swizzle puts that logical chunk
         const uint32_t expect = is_k ? k_off<D>(row, d0 / 8) : v_off<D>(row, d0 / 8);
         CHECK(expect == dst, "DMA slot mismatch w=%d i=%d p=%d", w, i, p);
@@ -99,13 +105,14 @@ static std::vector<long> dma_tile(bool is_k, int* worst64) {
   return tag;
 }
 
-template <int D>
+template <class C>
 static void check_lds() {
-  using TL = Tile<D>;
-  constexpr int BN = TL::BN;
+  constexpr int D = C::D;
+  constexpr int BN = C::BN;
+  constexpr uint32_t RB = C::rowBytes;
   int kw, vw;
-  const std::vector<long> ktag = dma_tile<D>(true, &kw);
-  const std::vector<long> vtag = dma_tile<D>(false, &vw);
+  const std::vector<long> ktag = dma_tile<C>(true, &kw);
+  const std::vector<long> vtag = dma_tile<C>(false, &vw);
 
   // ---- S^T operand reads
   int kr[2] = {1, 1};
@@ -114,13 +121,13 @@ static void check_lds() {
       std::vector<uint32_t> addr(64);
       for (int lane = 0; lane < 64; ++lane) {
         const uint32_t off = k_read_off<D>(kb, j, lane);
-        CHECK(off == k_read_off<D>(0, j, lane) + (uint32_t)(kb * 32 * TL::rowBytes),
+        CHECK(off == k_read_off<D>(0, j, lane) + (uint32_t)(kb * 32 * RB),
               "k_read_off not additive in kb");
         CHECK(off == (k_read_off<D>(0, 0, lane) ^ (uint32_t)(j << 5)) +
-                         (uint32_t)(kb * 32 * TL::rowBytes),
+                         (uint32_t)(kb * 32 * RB),
               "k_read_off is not step 0 XOR (j << 5)");
         addr[lane] = off;
-        CHECK(off % 16 == 0 && off + 16 <= (uint32_t)TL::bytes, "K read off %u", off);
+        CHECK(off % 16 == 0 && off + 16 <= (uint32_t)C::tileBytes, "K read off %u", off);
         const int key = 32 * kb + row_perm32(lane & 31);
         for (int e = 0; e < 8; ++e)
           CHECK(ktag[off / 2 + e] == tag_of(key, 16 * j + 8 * (lane >> 5) + e, D),
@@ -139,14 +146,14 @@ static void check_lds() {
         long src[64][4];
         for (int lane = 0; lane < 64; ++lane) {
           const uint32_t off = v_tr_off<D>(jd, kc, rd, lane);
-          CHECK(off == v_tr_off<D>(jd, 0, 0, lane) + (uint32_t)(kc * 16 * TL::rowBytes) +
-                           (uint32_t)(rd * 4 * TL::rowBytes),
+          CHECK(off == v_tr_off<D>(jd, 0, 0, lane) + (uint32_t)(kc * 16 * RB) +
+                           (uint32_t)(rd * 4 * RB),
                 "v_tr_off not additive in kc/rd");
           CHECK(off == (v_tr_off<D>(0, 0, 0, lane) ^ (uint32_t)(jd << 6)) +
-                           (uint32_t)(kc * 16 * TL::rowBytes) + (uint32_t)(rd * 4 * TL::rowBytes),
+                           (uint32_t)(kc * 16 * RB) + (uint32_t)(rd * 4 * RB),
                 "v_tr_off is not block 0 XOR (jd << 6)");
           addr[lane] = off;
-          CHECK(off % 8 == 0 && off + 8 <= (uint32_t)TL::bytes, "V read off %u", off);
+          CHECK(off % 8 == 0 && off + 8 <= (uint32_t)C::tileBytes, "V read off %u", off);
           for (int e = 0; e < 4; ++e) src[lane][e] = vtag[off / 2 + e];
         }
         for (int lane = 0; lane < 64; ++lane) {
@@ -172,22 +179,22 @@ static void check_lds() {
     }
   for (int r = 0; r < 32; ++r) CHECK(row_perm32(row_perm32(r)) == r, "perm involution");
 
-  std::printf("D=%d BN=%d tile=%d B: conflict degree (64 banks / 32 banks): K operand read %d/%d, "
-              "V^T transposed read %d/%d; DMA writes %d/%d (64 banks)\n",
-              D, BN, TL::bytes, kr[0], kr[1], vr[0], vr[1], kw, vw);
+  std::printf("D=%d waves=%d BN=%d tile=%d B: conflict degree (64 banks / 32 banks): K operand "
+              "read %d/%d, V^T transposed read %d/%d; DMA writes %d/%d (64 banks)\n",
+              D, C::NW, BN, C::tileBytes, kr[0], kr[1], vr[0], vr[1], kw, vw);
   CHECK(kr[0] == 1 && kr[1] == 1, "K operand reads conflict");
   CHECK(vr[0] == 1, "V^T reads conflict (64 banks)");
   CHECK(kw == 1 && vw == 1, "DMA writes conflict");
 }
 
-template <int D>
+template <class C>
 static void check_global(int B, int H, int S, bool causal) {
-  using TL = Tile<D>;
+  constexpr int D = C::D;
   const int BH = B * H;
-  const int nqt = num_q_tiles(S);
+  const int nqt = num_q_tiles(S, C::BM);
   const long grid = (long)nqt * BH;
-  constexpr int BN = TL::BN;
-  const uint32_t head_bytes = (uint32_t)S * TL::rowBytes;
+  constexpr int BN = C::BN;
+  const uint32_t head_bytes = (uint32_t)S * C::rowBytes;
   std::vector<char> seen(grid, 0);
   const size_t head_elems = (size_t)S * D;
   const bool track = head_elems * (size_t)BH <= ((size_t)1 << 26);
@@ -200,27 +207,27 @@ static void check_global(int B, int H, int S, bool causal) {
     const long cell = (long)qt * BH + bh;
     CHECK(!seen[cell], "tile visited twice");
     seen[cell] = 1;
-    const int kv_end = tile_kv_end(qt, S, causal);
+    const int kv_end = tile_kv_end(qt, S, causal, C::BM);
     const int ntiles = (kv_end + BN - 1) / BN;
     CHECK(ntiles >= 1 && (ntiles - 1) * BN < S, "tile count");
     // DMA sources: tile-relative offsets; rows past the end start at or past
     // the descriptor's range (S - kv0) * rowBytes
     for (int t = 0; t < ntiles; ++t) {
-      const uint32_t range = (uint32_t)(S - t * BN) * TL::rowBytes;
-      for (int w = 0; w < kWaves; ++w)
-        for (int i = 0; i < TL::dmaPerWave; ++i)
+      const uint32_t range = (uint32_t)(S - t * BN) * C::rowBytes;
+      for (int w = 0; w < C::NW; ++w)
+        for (int i = 0; i < C::dmaPerWave; ++i)
           for (int p = 0; p < 64; ++p)
             for (int kv = 0; kv < 2; ++kv) {
-              const uint32_t off = kv ? dma_src_v<D>(w, i, p) : dma_src_k<D>(w, i, p);
-              const int row = off / TL::rowBytes;
+              const uint32_t off = kv ? dma_src_v<C>(w, i, p) : dma_src_k<C>(w, i, p);
+              const int row = off / C::rowBytes;
               if (t * BN + row < S)
                 CHECK(off + 16 <= range, "DMA in-range row crosses the end");
               else
                 CHECK(off >= range, "DMA row past S not wholly out of range");
             }
     }
-    for (int wave = 0; wave < kWaves; ++wave) {
-      const int q0w = qt * kBM + wave * kRowsPerWave;
+    for (int wave = 0; wave < C::NW; ++wave) {
+      const int q0w = qt * C::BM + wave * kRowsPerWave;
       const bool live = q0w < S;
       const int nw = live ? (wave_kv_end(q0w, S, causal) + BN - 1) / BN : 0;
       CHECK(nw <= ntiles, "wave computes a tile the work-group does not load");
@@ -275,23 +282,139 @@ static void check_global(int B, int H, int S, bool causal) {
   }
 }
 
+// ------------------------------------------------ ping-pong schedule replay
+// One DMA share (one wave's issues) of a tile into a stage.
+struct Share {
+  int issue_slot;  // slot in which it was issued
+  int land_slot;   // end of this slot: the issuing wave has waited for it
+                   // (-1: before slot 0; kNotLanded: not yet)
+};
+constexpr int kNotLanded = -1000;
+struct Stage {
+  int tile = -2;  // tile the stage holds (-1: zeros of an empty range)
+  std::vector<Share> shares;
+};
+
+// Replays the slots of both groups of the eight-wave kernel for a work-group
+// with `ntiles` KV tiles and waves that compute `nw` of them, mirroring the
+// kernel's code order, and checks every read and every overwrite.
+static void check_pingpong(int ntiles, int nw) {
+  const int NS = kStages;
+  Stage kst[3], vst[3];
+  // pending DMA per group: (array, stage index) of each share of the latest
+  // pairs not yet waited for, in issue order; a wait for all but the latest
+  // pair lands everything older.
+  struct Pend { Stage* st; size_t share; int pair; };
+  std::vector<Pend> pend[2];
+  int last_pair[2] = {-100, -100};
+  // reads in each slot, for the overwrite check: (array, stage, tile)
+  std::map<int, std::vector<std::pair<Stage*, int>>> reads;
+
+  auto issue = [&](int g, Stage* st, int tile, int slot, int pair) {
+    if (st->shares.size() == 2) {  // both groups' shares of the old content
+      // no read of the old content may happen in or after this slot
+      for (auto& kv : reads)
+        if (kv.first >= slot)
+          for (auto& r : kv.second)
+            CHECK(!(r.first == st && r.second == st->tile), "stage overwritten while read");
+      st->shares.clear();
+      st->tile = tile;
+    } else if (st->shares.empty()) {
+      st->tile = tile;
+    } else {
+      CHECK(st->tile == tile, "the two groups DMA different tiles into one stage");
+    }
+    st->shares.push_back({slot, kNotLanded});
+    pend[g].push_back({st, st->shares.size() - 1, pair});
+  };
+  auto wait_all_but_latest = [&](int g, int slot) {
+    std::vector<Pend> keep;
+    for (auto& p : pend[g]) {
+      if (p.pair == last_pair[g]) keep.push_back(p);
+      else p.st->shares[p.share].land_slot = slot;
+    }
+    pend[g] = keep;
+  };
+  auto wait_all = [&](int g, int slot) {
+    for (auto& p : pend[g]) p.st->shares[p.share].land_slot = slot;
+    pend[g].clear();
+  };
+  auto read = [&](Stage* st, int tile, int slot) {
+    CHECK(st->tile == tile, "slot %d reads tile %d but the stage holds %d", slot, tile, st->tile);
+    CHECK(st->shares.size() == 2, "slot %d reads a stage only one group has filled", slot);
+    for (auto& sh : st->shares)
+      CHECK(sh.land_slot != kNotLanded && sh.land_slot < slot, "slot %d reads tile %d before it landed",
+            slot, tile);
+    reads[slot].push_back({st, tile});
+  };
+  auto dma_pair = [&](int g, int i, int slot) {
+    last_pair[g] = i;
+    issue(g, &kst[(i + 2) % NS], i + 2 < ntiles ? i + 2 : -1, slot, i);
+    issue(g, &vst[(i + 1) % NS], i + 1 < ntiles ? i + 1 : -1, slot, i);
+  };
+
+  // prologue (both groups, waited with vmcnt(0) before the first barrier)
+  for (int g = 0; g < 2; ++g) {
+    issue(g, &kst[0], 0, -1, -1);
+    issue(g, &kst[1], ntiles > 1 ? 1 : -1, -1, -1);
+    issue(g, &kst[2], -1, -1, -1);
+    issue(g, &vst[0], 0, -1, -1);
+    issue(g, &vst[1], -1, -1, -1);
+    issue(g, &vst[2], -1, -1, -1);
+    wait_all(g, -1);
+  }
+  // Both groups advance slot by slot; the slot numbers of each group's code
+  // follow the kernel: A runs step j in (2j, 2j+1), B in (2j+1, 2j+2).
+  const int nslots = 2 * ntiles + 3;
+  for (int t = 0; t < nslots; ++t) {
+    for (int g = 0; g < 2; ++g) {
+      const int local = t - g;  // B's slot 0 is its lone DMA slot
+      if (g == 1 && t == 0) {
+        dma_pair(1, 0, t);
+      } else if (g == 0 && t == nslots - 1) {
+        // A's lone last slot
+      } else {
+        const int j = local / 2;
+        if (local % 2 == 0) {  // MFMA phase of step j
+          if (g == 0) dma_pair(0, j, t);
+          if (j >= 1 && j - 1 < nw) read(&vst[(j + 2) % NS], j - 1, t);
+          if (j < nw) read(&kst[j % NS], j, t);
+        } else {  // softmax phase of step j
+          if (g == 1) dma_pair(1, j + 1, t);
+        }
+      }
+    }
+    for (int g = 0; g < 2; ++g) wait_all_but_latest(g, t);
+  }
+  for (int g = 0; g < 2; ++g) wait_all(g, nslots);
+  CHECK(pp_slots(ntiles) + 1 == nslots, "slot count");
+}
+
 int main() {
-  check_lds<64>();
-  check_lds<128>();
+  check_lds<Cfg4<64>>();
+  check_lds<Cfg4<128>>();
+  check_lds<Cfg8<64>>();
+  check_lds<Cfg8<128>>();
+  for (int ntiles = 1; ntiles <= 12; ++ntiles)
+    for (int nw = 0; nw <= ntiles; ++nw) check_pingpong(ntiles, nw);
+  std::printf("ping-pong schedule: ntiles 1..12, every wave tile count: checked\n");
   const int shapes[][3] = {{1, 1, 1}, {1, 1, 7}, {1, 1, 64}, {1, 1, 127}, {1, 1, 128},
                            {1, 1, 129}, {1, 2, 200}, {2, 3, 255}, {2, 3, 300}, {1, 1, 1000},
                            {1, 16, 1024}, {1, 1, 4097}};
   for (auto& s : shapes)
     for (int causal = 0; causal < 2; ++causal) {
-      check_global<64>(s[0], s[1], s[2], causal);
-      check_global<128>(s[0], s[1], s[2], causal);
+      check_global<Cfg4<64>>(s[0], s[1], s[2], causal);
+      check_global<Cfg4<128>>(s[0], s[1], s[2], causal);
+      check_global<Cfg8<64>>(s[0], s[1], s[2], causal);
+      check_global<Cfg8<128>>(s[0], s[1], s[2], causal);
     }
   // full-size shapes (O coverage tracked up to 64M elements)
-  check_global<64>(1, 16, 1024, true);
-  check_global<64>(10, 64, 1024, false);
-  check_global<128>(2, 16, 8192, true);
-  check_global<128>(1, 8, 16384, true);
-  check_global<128>(1, 1, 65536, true);
+  check_global<Cfg4<64>>(1, 16, 1024, true);
+  check_global<Cfg8<64>>(10, 64, 1024, false);
+  check_global<Cfg8<128>>(2, 16, 8192, true);
+  check_global<Cfg8<128>>(1, 8, 16384, true);
+  check_global<Cfg4<128>>(1, 1, 65536, true);
+  check_global<Cfg8<128>>(1, 1, 65536, true);
   if (g_err) {
     std::printf("FAILED with %d errors\n", g_err);
     return 1;

@@ -47,20 +47,25 @@ def test_kernel_launch_stubs_are_defined():
         pytest.skip("no nm")
     out = subprocess.run([nm, "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
     stubs = [l for l in out.splitlines() if "device_stub" in l]
-    assert len(stubs) == 24
+    # 2 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic thresholds)
+    assert len(stubs) == 48
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 100
+    assert fa.fa_version() == 200
     for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG):
         assert fa.fa_strerror(st) and fa.fa_strerror(st) != "unknown status"
     assert fa.fa_strerror(12345) == "unknown status"
 
 
 def test_tile_query():
-    assert fa.fa_fwd_tile(128, 2, 16, 8192) == (128, 64, 256, 2 * 16 * 64)
-    assert fa.fa_fwd_tile(64, 10, 64, 1024) == (128, 64, 256, 640 * 8)
+    # eight-wave kernel once B*H*ceil(S/256) >= 256 work-groups, else four-wave
+    assert fa.fa_fwd_tile(128, 2, 16, 8192) == (256, 64, 512, 2 * 16 * 32)
+    assert fa.fa_fwd_tile(64, 10, 64, 1024) == (256, 128, 512, 640 * 4)
+    assert fa.fa_fwd_tile(64, 1, 16, 1024) == (128, 64, 256, 16 * 8)
+    assert fa.fa_fwd_tile(128, 1, 64, 1024) == (256, 64, 512, 256)
+    assert fa.fa_fwd_tile(128, 1, 63, 1024) == (128, 64, 256, 63 * 8)
     assert fa.fa_fwd_tile(64, 1, 1, 129)[3] == 2
     with pytest.raises(fa.FaError):
         fa.fa_fwd_tile(96)
@@ -117,11 +122,15 @@ def test_typed_wrappers_validate_the_same_way():
 def test_diag_validation():
     a = GOOD
     args = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 8, 64, 0, 0.1, None, 0)
-    assert fa.fa_fwd_diag(*args, 3, 0x20000000000, check=False) == ARG
-    assert fa.fa_fwd_diag(*args, 8, 0, check=False) == NULL
-    assert fa.fa_fwd_diag(*args, 0, 0x20000000004, check=False) == ALIGN
+    ev = 0x20000000000
+    assert fa.fa_fwd_diag(*args, 3, 0, ev, check=False) == ARG
+    assert fa.fa_fwd_diag(*args, 8, 3, ev, check=False) == ARG
+    assert fa.fa_fwd_diag(*args, 8, -1, ev, check=False) == ARG
+    assert fa.fa_fwd_diag(*args, 8, 0, 0, check=False) == NULL
+    assert fa.fa_fwd_diag(*args, 0, 2, ev + 4, check=False) == ALIGN
     e = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 0, 64, 0, 0.1, None, 0)
-    assert fa.fa_fwd_diag(*e, 8, 0x20000000000, check=False) == OK
+    for variant in (0, 1, 2):
+        assert fa.fa_fwd_diag(*e, 8, variant, ev, check=False) == OK
 
 
 def test_error_raises_with_name():

@@ -23,8 +23,11 @@ def _banner(msg):
     print(msg, flush=True)
 
 
-def _check_full(qb, kb, vb, dtype, causal, scale, tag):
-    o, lse = run(qb, kb, vb, dtype, causal, scale)
+VARIANTS = {"k4": fa.VARIANT_FOUR_WAVE, "pp": fa.VARIANT_PING_PONG}
+
+
+def _check_full(qb, kb, vb, dtype, causal, scale, tag, variant=None):
+    o, lse = run(qb, kb, vb, dtype, causal, scale, variant=variant)
     og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
     B, H, S, _ = qb.shape
     eo, el = compare_rows(qb, kb, vb, dtype, causal, scale, og, lg,
@@ -43,17 +46,44 @@ def test_tiny_workload(causal):
     _check_full(*W.make_inputs(w), w.dtype, causal, w.scale, f"tiny causal={causal}")
 
 
+@pytest.mark.parametrize("kernel", ["k4", "pp"])
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("S", [1, 7, 64, 129, 300])
-def test_small_shapes_all_rows(S, causal, D, dtype):
-    """Several Q and KV tiles, ragged tails, tiny S; every output compared."""
+def test_small_shapes_all_rows(S, causal, D, dtype, kernel):
+    """Several Q and KV tiles, ragged tails, tiny S; every output compared;
+    each shape through both kernels."""
     shape = (2, 3, S, D)
     seed = 1000 + S * 4 + D + (dtype == W.BF16) * 2 + causal
     qb, kb, vb = (W.random_bits(shape, dtype, seed + i) for i in range(3))
     _check_full(qb, kb, vb, dtype, causal, 1.0 / math.sqrt(D),
-                f"S={S} D={D} {dtype} causal={causal}")
+                f"S={S} D={D} {dtype} causal={causal} kernel={kernel}", VARIANTS[kernel])
+
+
+@pytest.mark.parametrize("kernel", ["k4", "pp"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_tiles_all_rows(causal, D, kernel):
+    """Many KV tiles per work-group (every stage of both pipelines reused
+    several times, the three-stage ring wrapping), a ragged end, all rows."""
+    S, dt = 1500, W.BF16
+    shape = (1, 2, S, D)
+    qb, kb, vb = (W.random_bits(shape, dt, 2000 + D + causal + i) for i in range(3))
+    _check_full(qb, kb, vb, dt, causal, 1.0 / math.sqrt(D),
+                f"many tiles S={S} D={D} causal={causal} kernel={kernel}", VARIANTS[kernel])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_kernels_agree(D):
+    """Both kernels on one input: each within tolerance of the oracle and of
+    each other (they differ only in tile sizes, hence rescale points)."""
+    S, dt = 777, W.F16
+    qb, kb, vb = (W.random_bits((2, 2, S, D), dt, 3000 + D + i) for i in range(3))
+    res = [_check_full(qb, kb, vb, dt, True, D ** -0.5, f"agree D={D} {k}", VARIANTS[k])
+           for k in ("k4", "pp")]
+    assert np.abs(res[0][0] - res[1][0]).max() <= O_TOL[dt]
+    assert np.abs(res[0][1] - res[1][1]).max() <= LSE_TOL
 
 
 # full-size workloads, sampled rows (the oracle computes each row on its own)
@@ -162,7 +192,7 @@ def test_large_logits_do_not_overflow(dtype):
 
 # -------------------------------------------------------- lazy vs eager rescale
 
-def _diag(qb, kb, vb, dtype, causal, scale, thr):
+def _diag(qb, kb, vb, dtype, causal, scale, thr, variant=0):
     q, k, v = (to_dev(x, dtype) for x in (qb, kb, vb))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device())
@@ -170,20 +200,22 @@ def _diag(qb, kb, vb, dtype, causal, scale, thr):
     B, H, S, D = q.shape
     fa.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                    B, H, S, D, causal, scale, torch.cuda.current_stream().cuda_stream,
-                   W.DTYPE_CODE[dtype], thr, ev.data_ptr())
+                   W.DTYPE_CODE[dtype], thr, variant, ev.data_ptr())
     torch.cuda.synchronize()
     return o_to_f64(o), lse.cpu().numpy().astype(np.float64), int(ev.item())
 
 
+@pytest.mark.parametrize("kernel", ["k4", "pp"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_lagging_and_eager_rescale_both_match(D):
+def test_lagging_and_eager_rescale_both_match(D, kernel):
     """Threshold 8 (production) and 0 (eager) both meet tolerance on a steep
     key ramp; the lag cuts rescale events; event counts track the float64
     model of the same algorithm with the same KV tile size."""
     dt = W.BF16
     w = W.Workload("steep", 1, 2, 2048, D, dt, True, 21, ramp=0.05)
     qb, kb, vb = W.make_inputs(w)
-    res = {thr: _diag(qb, kb, vb, dt, True, w.scale, thr) for thr in (8, 0)}
+    variant = VARIANTS[kernel]
+    res = {thr: _diag(qb, kb, vb, dt, True, w.scale, thr, variant) for thr in (8, 0)}
     plan = [((0, h), sample_rows(w.S, 128, seed=h)) for h in range(w.H)]
     for thr, (og, lg, ev) in res.items():
         eo, el = compare_rows(qb, kb, vb, dt, True, w.scale, og, lg, plan)
@@ -191,11 +223,13 @@ def test_lagging_and_eager_rescale_both_match(D):
         assert eo <= O_TOL[dt] and el <= LSE_TOL
     lazy, eager = res[8][2], res[0][2]
     assert 0 < lazy < eager
-    # production result equals fa_fwd bit for bit (same arithmetic, counter aside)
-    o, lse = run(qb, kb, vb, dt, True, w.scale)
-    np.testing.assert_array_equal(o_to_f64(o), res[8][0])
+    # the production instantiation of the same kernel gives the same bits
+    # (same arithmetic, counter aside)
+    o, lse = run(qb, kb, vb, dt, True, w.scale, variant=None)
+    if fa.fa_fwd_tile(D, w.B, w.H, w.S)[0] == (256 if kernel == "pp" else 128):
+        np.testing.assert_array_equal(o_to_f64(o), res[8][0])
     # the float64 model of the algorithm, same KV tile size
-    bn = fa.fa_fwd_tile(D)[1]
+    bn = 128 if (kernel == "pp" and D == 64) else 64
     model = {8: 0, 0: 0}
     for h in range(w.H):
         q, k, v = (W.decode(x[0, h], dt) for x in (qb, kb, vb))
@@ -218,8 +252,9 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("kernel", ["k4", "pp"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_no_writes_outside_outputs(D):
+def test_no_writes_outside_outputs(D, kernel):
     """Outputs embedded in guard bands: the kernel writes only O and lse."""
     B, H, S, dt = 1, 3, 200, W.F16
     qb, kb, vb = (W.random_bits((B, H, S, D), dt, 40 + i) for i in range(3))
@@ -229,8 +264,10 @@ def test_no_writes_outside_outputs(D):
     lbuf = torch.full((nl + 2 * g,), -3.0, dtype=torch.float32, device=device())
     o = obuf[g:g + n]
     lse = lbuf[g:g + nl]
-    fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, S, D,
-              1, D ** -0.5, torch.cuda.current_stream().cuda_stream, fa.FA_F16)
+    ev = torch.zeros(1, dtype=torch.int64, device=device())
+    fa.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                   S, D, 1, D ** -0.5, torch.cuda.current_stream().cuda_stream, fa.FA_F16, 8,
+                   VARIANTS[kernel], ev.data_ptr())
     torch.cuda.synchronize()
     assert torch.all(obuf[:g] == 7.0) and torch.all(obuf[g + n:] == 7.0)
     assert torch.all(lbuf[:g] == -3.0) and torch.all(lbuf[g + nl:] == -3.0)
