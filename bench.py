@@ -15,7 +15,10 @@ configuration the metric is quoted on). FLOPs follow the metric:
 
 Extra modes (used to take profiles): --calibrate-copy runs plain device
 copies of a known size first (for scaling HBM byte counters);
---no-cpu-baseline skips the oracle leg.
+--no-cpu-baseline skips the oracle leg; --write-traffic FETCH_CSV WRITE_CSV
+(no GPU needed) turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE,
+each of a --calibrate-copy bench run) into the per-launch HBM traffic file
+that fills roofline.traffic.
 """
 from __future__ import annotations
 
@@ -61,6 +64,59 @@ def load_traffic(workload: str):
     if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
+
+
+CALIBRATION_BYTES = 1 << 30  # each --calibrate-copy copy reads and writes 1 GiB
+
+
+def kernel_name(w) -> str:
+    """The kernel fa_fwd launches for this workload (from the tile query)."""
+    import exact_attention_16_amd as fa
+    bm, bn, threads, groups = fa.fa_fwd_tile(w.D, w.B, w.H, w.S)
+    kind = "fa_fwd_pp" if threads == 512 else "fa_fwd_k4"
+    return (f"{kind}<{w.dtype},D={w.D},causal={int(w.causal)}> "
+            f"({groups} work-groups x {threads} threads, {bm} query rows, {bn}-key tiles)")
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> dict:
+    """Per-launch HBM bytes of the attention kernel from two rocprofv3 --pmc
+    counter files. FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is
+    scaled by the ratio of the known size of the plain 1 GiB device copies
+    that --calibrate-copy runs to what the same counter reads for them."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = r["Dispatch_Id"]
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            prev = rows.get(key, (name, 0.0))
+            rows[key] = (name, prev[1] + v)
+        copies = [v for n, v in rows.values() if "copyBuffer" in n and v > 1e5]
+        attn = [v for n, v in rows.values() if "fa_fwd_" in n]
+        names = sorted({n for n, _ in rows.values() if "fa_fwd_" in n})
+        if not copies or not attn:
+            raise SystemExit(f"{path}: no calibration copies or attention dispatches for {counter}")
+        factor = CALIBRATION_BYTES / (sum(copies) / len(copies) * 1024.0)
+        return factor, sum(attn) / len(attn), len(attn), names
+
+    ff, fkib, fn, names = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wf, wkib, wn, _ = per_dispatch(write_csv, "WRITE_SIZE")
+    out = {
+        "source_hash": kernel_source_hash(),
+        "workload": workload,
+        "kernels": names,
+        "fetch_kib_per_dispatch": fkib, "fetch_dispatches": fn, "fetch_scale": ff,
+        "write_kib_per_dispatch": wkib, "write_dispatches": wn, "write_scale": wf,
+        "bytes_per_launch": fkib * 1024.0 * ff + wkib * 1024.0 * wf,
+        "note": "scale = 1 GiB / (counter KiB x 1024) of the calibration copies",
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def blas_threads() -> int:
@@ -131,7 +187,13 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run plain 1 GiB device copies first (counter scaling)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic file from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
+
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic, args.workload), indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); "
@@ -211,7 +273,7 @@ def main(argv=None) -> int:
     traffic = load_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_TFLOPS, "traffic": traffic,
-                "kernel": f"fa_fwd_kernel<{w.dtype},D={w.D},causal={int(w.causal)}>",
+                "kernel": kernel_name(w),
                 "flops_per_launch": w.flops, "avg_launch_ms": ms_per_step,
                 "median_launch_ms": med_ms, "algorithmic_bytes_per_launch": bytes_alg}
 

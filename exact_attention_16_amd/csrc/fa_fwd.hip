@@ -41,11 +41,11 @@
 // lower-triangle causal mask (xdnf.cn, "CUDA手写masked multi-head attention
 // 性能优化实战", 3.1); tiling with running max/sum, v2 loop order, deferred
 // normalisation and the (Q tile, head) grid (hotdry.top, "FlashAttention的
-// Triton性能考古学", "核心算法回顾" and "FlashAttention v2"); the conditional
-// rescale with a lag of 8 and p in (0, 256], the warp-vote skip of the
-// rescale, the rescale done by the softmax workers themselves, and issuing
-// the next tile's Q.K^T ahead of the current P.V (hjcheng0602.cn, "Flash
-// Attention CUDA Kernel 优化 ... G6", V39, V41 and V44).
+// Triton性能考古学", sections "核心算法回顾" and "FlashAttention v2：循环重构与
+// 寄存器积累"); the conditional rescale with a lag of 8 and p in (0, 256], the
+// warp-vote skip of the rescale, the rescale done by the softmax workers
+// themselves, and issuing the next tile's Q.K^T ahead of the current P.V
+// (hjcheng0602.cn, "Flash Attention CUDA Kernel 优化 ... G6", V39, V41, V44).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -150,6 +150,21 @@ template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0x0070 | N);
 }
 
+// Scheduling pattern for one region: DS0 LDS reads up front, then REPS
+// times {one MFMA, V1 VALU, DS LDS reads, one MFMA, V2 VALU}.
+template <int DS0, int REPS, int V1, int DS, int V2>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+  for (int i = 0; i < REPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V2, 0);
+  }
+}
+
 // One wave's share of a work-group: its query rows, accumulators and the
 // per-tile operations on them.
 template <typename T, class C, bool CAUSAL, int THR, bool DIAG>
@@ -173,8 +188,9 @@ struct Wave {
   float b, lsum;
   unsigned n_events;
 
+  // sub: which 32-row block of the wave's C::RPW rows this object holds
   __device__ __forceinline__ void init(const T* Q, const T* K, const T* V, int BH, int S_, int nqt,
-                                       float c_) {
+                                       float c_, int sub = 0) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -185,7 +201,7 @@ struct Wave {
     const size_t head = (size_t)bh * (size_t)S * D;
     Kh = K + head;
     Vh = V + head;
-    q0w = qt * C::BM + wave * kRowsPerWave;
+    q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
     qrow = q0w + (lane & 31);
     // Q operand fragments (rows past S read as zeros)
     const auto rq = FA_RSRC(Q + head, (uint32_t)S * RB);
@@ -211,6 +227,14 @@ struct Wave {
   }
   __device__ __forceinline__ int group_tiles() const {
     return (tile_kv_end(qt, S, CAUSAL, C::BM) + BN - 1) / BN;
+  }
+
+  // Leading KV tiles that need no index compares for these rows: tiles
+  // before the one holding key q0w (causal) and before the ragged end.
+  __device__ __forceinline__ int unmasked_tiles() const {
+    const int r = S / BN;
+    const int d = q0w / BN;
+    return CAUSAL ? (d < r ? d : r) : r;
   }
 
   // this wave's share of the DMA of K or V tile t into an LDS stage; a tile
@@ -463,6 +487,169 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   w.epilogue(O, LSE, events);
 }
 
+// ------------------------------------------------- four waves x 64 rows
+// Each wave holds two 32-row blocks A and B. Per 32-key tile j, in program
+// order (one scheduling region each, so the compiler interleaves the two
+// independent streams):
+//   part a: S_A(j), S_B(j) = K(j) Q^T (each K fragment read once, two MFMAs)
+//           with block B's exponentials of tile j-1 -> P_B(j-1)
+//   part b: O_A += P_A(j-1) V(j-1), O_B += P_B(j-1) V(j-1) (each V fragment
+//           read once) with block A's softmax of tile j -> P_A(j) and block
+//           B's tile max of tile j (its new base applies from part a on)
+//   then the rare O rescales, a wait for the DMA and one barrier.
+// K and V tiles use three LDS stages, issued two tiles ahead as in the
+// eight-wave kernel.
+template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_fwd_w2(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+          T* __restrict__ O, float* __restrict__ LSE, int BH, int S, int nqt, float c,
+          unsigned long long* __restrict__ events) {
+  using C = CfgW2<D>;
+  using W = Wave<T, C, CAUSAL, THR, DIAG>;
+  constexpr int TB = C::tileBytes;
+  constexpr int DPW = C::dmaPerWave;
+  constexpr int NKB = W::NKB, NKC = W::NKC, NDC = W::NDC, NDB = W::NDB;
+  constexpr uint32_t RB = C::rowBytes;
+  static_assert(kStages == 3, "the step below is unrolled over three stages");
+  __shared__ __attribute__((aligned(1024))) char ks0[TB];
+  __shared__ __attribute__((aligned(1024))) char ks1[TB];
+  __shared__ __attribute__((aligned(1024))) char ks2[TB];
+  __shared__ __attribute__((aligned(1024))) char vs0[TB];
+  __shared__ __attribute__((aligned(1024))) char vs1[TB];
+  __shared__ __attribute__((aligned(1024))) char vs2[TB];
+  lds_char* const lk0 = (lds_char*)ks0;
+  lds_char* const lk1 = (lds_char*)ks1;
+  lds_char* const lk2 = (lds_char*)ks2;
+  lds_char* const lv0 = (lds_char*)vs0;
+  lds_char* const lv1 = (lds_char*)vs1;
+  lds_char* const lv2 = (lds_char*)vs2;
+
+  W wa, wb;
+  wa.init(Q, K, V, BH, S, nqt, c, 0);
+  wb.init(Q, K, V, BH, S, nqt, c, 1);
+  const int ntiles = wa.group_tiles();
+  // tiles either block computes (block B's rows can lie wholly past S)
+  const int nlast = max(wa.wave_tiles(), wb.wave_tiles());
+  const int nfull = wa.unmasked_tiles();  // tiles before this is < both blocks' first masked
+
+  // Double buffers, alternating by iteration parity: S_B(j-1) / S_B(j) and
+  // P_A(j-1) / P_A(j). Before the first tile S_B = -inf and P_A = 0, so that
+  // iteration 0 runs the same code (its block-B exponentials give P_B = 0
+  // and its P.V adds zeros from the zero-filled stage).
+  f32x16 sA[NKB], sB0[NKB], sB1[NKB];
+  u32x4 pA0[NKC], pA1[NKC], pB[NKC];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) sB0[kb] = (f32x16){} - INFINITY;
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) pA0[kc] = (u32x4){};
+
+  // both blocks' S for the K tile at kt: one LDS read per fragment
+  auto qk2 = [&](const lds_char* kt, f32x16 (&sb)[NKB]) {
+#pragma unroll
+    for (int j = 0; j < NDC; ++j) {
+      const lds_char* base = kt + (wa.koff0 ^ (uint32_t)(j << 5));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const u32x4 kf = lds16(base + kb * 32 * RB);
+        sA[kb] = Ops<T>::mfma(kf, wa.qf[j], j == 0 ? (f32x16){} : sA[kb]);
+        sb[kb] = Ops<T>::mfma(kf, wb.qf[j], j == 0 ? (f32x16){} : sb[kb]);
+      }
+    }
+  };
+  // both blocks' O for the V tile at vt: one LDS read per fragment
+  auto pv2 = [&](const lds_char* vt, const u32x4 (&pa)[NKC]) {
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int jd = 0; jd < NDB; ++jd) {
+        const u32x4 vf =
+            lds_tr_pair(vt + (wa.voff0 ^ (uint32_t)(jd << 6)) + kc * 16 * RB, 4 * RB);
+        wa.o[jd] = Ops<T>::mfma(vf, pa[kc], wa.o[jd]);
+        wb.o[jd] = Ops<T>::mfma(vf, pB[kc], wb.o[jd]);
+      }
+  };
+  auto dma_pair = [&](auto r, int i) {
+    constexpr int R = decltype(r)::value;
+    wa.dma_k(pick3<(R + 2) % 3>(lk0, lk1, lk2), i + 2, ntiles);
+    wa.dma_v(pick3<(R + 1) % 3>(lv0, lv1, lv2), i + 1, ntiles);
+  };
+
+  // prologue: K(0), K(1), V(0); the other stages get empty ranges (zeros),
+  // which also gives the compiler a DMA into every stage from the first
+  // block on
+  wa.dma_k(lk0, 0);
+  wa.dma_k(lk1, 1, ntiles);
+  wa.dma_k(lk2, 2, 0);
+  wa.dma_v(lv0, 0);
+  wa.dma_v(lv1, 1, 0);
+  wa.dma_v(lv2, 2, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
+
+  // Iteration j = 0 .. ntiles (R = j mod 3, P = j mod 2): K(j) in stage R,
+  // V(j-1) in stage R-1. Tiles a block cannot see at all are masked to
+  // -inf like any other, giving p = 0; a wave past its last tile only
+  // issues its DMA share and meets the barrier.
+  auto step = [&](auto r, auto par, int j) {
+    constexpr int R = decltype(r)::value;
+    constexpr int P = decltype(par)::value;
+    f32x16(&sBo)[NKB] = pick<P>(sB1, sB0);  // S_B(j-1)
+    f32x16(&sBn)[NKB] = pick<P>(sB0, sB1);  // S_B(j)
+    u32x4(&pAo)[NKC] = pick<P>(pA1, pA0);   // P_A(j-1)
+    u32x4(&pAn)[NKC] = pick<P>(pA0, pA1);   // P_A(j)
+    dma_pair(r, j);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j <= nlast) {
+      // part a: S_A(j), S_B(j); block B's exponentials of tile j-1. P_B
+      // and B's row sum are pinned here, beside the MFMAs they overlap.
+      qk2(pick3<R>(lk0, lk1, lk2), sBn);
+      wb.softmax_exp(sBo, pB);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(pB[kc]));
+      asm volatile("" : "+v"(wb.lsum));
+      interleave<2, NDC * NKB, 4, 1, 4>();
+      if (j >= nfull) {
+        const int kv0 = j * W::BN;
+        wa.mask(sA, kv0);
+        wb.mask(sBn, kv0);
+      }
+      // part b: P.V of tile j-1 for both blocks; block A's softmax of tile
+      // j; block B's max of tile j
+      pv2(pick3<(R + 2) % 3>(lv0, lv1, lv2), pAo);
+      const float hA = wa.softmax_max(sA);
+      wa.softmax_exp(sA, pAn);
+      const float hB = wb.softmax_max(sBn);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(pAn[kc]));
+      asm volatile("" : "+v"(wa.lsum));
+      interleave<4, NKC * NDB, 6, 2, 6>();
+      // rare: move O to the new bases (after this P.V, before the next)
+      wa.rescale(j, hA);
+      wb.rescale(j, hB);
+    }
+    wait_vm_lgkm0<2 * DPW>();
+    wg_barrier();
+  };
+  for (int j = 0;; j += 6) {
+    step(IC<0>{}, IC<0>{}, j);
+    if (j + 1 > ntiles) break;
+    step(IC<1>{}, IC<1>{}, j + 1);
+    if (j + 2 > ntiles) break;
+    step(IC<2>{}, IC<0>{}, j + 2);
+    if (j + 3 > ntiles) break;
+    step(IC<0>{}, IC<1>{}, j + 3);
+    if (j + 4 > ntiles) break;
+    step(IC<1>{}, IC<0>{}, j + 4);
+    if (j + 5 > ntiles) break;
+    step(IC<2>{}, IC<1>{}, j + 5);
+    if (j + 6 > ntiles) break;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the work-group
+  wa.epilogue(O, LSE, events);
+  wb.epilogue(O, LSE, events);
+}
+
 // ------------------------------------------------------------ four-wave
 // Register pipeline depth per head dimension. D=64: three stages (S(j+1),
 // P(j-1).V(j-1) and softmax(j) in one block) fit two waves per SIMD. D=128:
@@ -593,7 +780,7 @@ fa_fwd_k4(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
 // one work-group per compute unit, else the four-wave kernel.
 constexpr long long kPingPongMinGroups = 256;
 
-enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2 };
+enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kTwoBlock = 3 };
 
 template <int D> static bool use_pingpong(int BH, int S, int variant) {
   if (variant == kFourWave) return false;
@@ -607,7 +794,12 @@ static int launch_one(const void* q, const void* k, const void* v, void* o, floa
                       int variant) {
   const int BH = B * H;
   const float c = scale * kLog2e;
-  if (use_pingpong<D>(BH, S, variant)) {
+  if (variant == kTwoBlock) {
+    const int nqt = num_q_tiles(S, CfgW2<D>::BM);
+    hipLaunchKernelGGL((fa_fwd_w2<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)nqt * (unsigned)BH),
+                       dim3(CfgW2<D>::threads), 0, stream, (const T*)q, (const T*)k, (const T*)v,
+                       (T*)o, lse, BH, S, nqt, c, ev);
+  } else if (use_pingpong<D>(BH, S, variant)) {
     const int nqt = num_q_tiles(S, Cfg8<D>::BM);
     hipLaunchKernelGGL((fa_fwd_pp<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)nqt * (unsigned)BH),
                        dim3(Cfg8<D>::threads), 0, stream, (const T*)q, (const T*)k, (const T*)v,
@@ -706,7 +898,7 @@ int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse
   const int st = fa::validate(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, &empty);
   if (st != FA_OK) return st;
   if (threshold_log2 != 0 && threshold_log2 != 8) return FA_ERR_ARG;
-  if (variant < fa::kAuto || variant > fa::kPingPong) return FA_ERR_ARG;
+  if (variant < fa::kAuto || variant > fa::kTwoBlock) return FA_ERR_ARG;
   if (!rescale_events) return FA_ERR_NULL;
   if (((uintptr_t)rescale_events & 7) != 0) return FA_ERR_ALIGN;
   if (empty) return FA_OK;

@@ -8,8 +8,9 @@
 //
 // Notation follows the pages: a work-group owns one block of query rows
 // (a "Q tile", Br rows) of one (batch, head) and streams key/value blocks
-// ("KV tiles", Bc keys) past it (hotdry.top, "FlashAttention的Triton性能
-// 考古学", sections on the v2 loop order and the (cdiv(S, Bc), B*N_h) grid).
+// ("KV tiles", Bc keys) past it, one work-group per (Q tile, batch*head)
+// (hotdry.top, "FlashAttention的Triton性能考古学", section "FlashAttention
+// v2：循环重构与寄存器积累": the loop order and the grid).
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -25,15 +26,17 @@ namespace fa {
 constexpr int kRowsPerWave = 32;  // query rows owned by one wave (one MFMA column block)
 
 // A kernel configuration: head dimension D, NW waves (64 lanes) per
-// work-group, BN keys per KV tile. One K or V tile in LDS holds BN rows
-// (keys) of D 16-bit elements, row-major, each row split in 16-byte chunks
-// whose order is XOR-swizzled per row.
-template <int D_, int NW_, int BN_> struct Cfg {
+// work-group, BN keys per KV tile, RPW query rows per wave (one or two
+// 32-row MFMA column blocks). One K or V tile in LDS holds BN rows (keys) of
+// D 16-bit elements, row-major, each row split in 16-byte chunks whose order
+// is XOR-swizzled per row.
+template <int D_, int NW_, int BN_, int RPW_ = kRowsPerWave> struct Cfg {
   static constexpr int D = D_;
   static constexpr int NW = NW_;
   static constexpr int BN = BN_;
+  static constexpr int RPW = RPW_;
   static constexpr int threads = 64 * NW;
-  static constexpr int BM = kRowsPerWave * NW;           // query rows per work-group
+  static constexpr int BM = RPW * NW;                    // query rows per work-group
   static constexpr int rowBytes = D * 2;
   static constexpr int chunks = D / 8;                   // 16-byte chunks per row
   static constexpr int tileBytes = BN * rowBytes;        // one K or V tile
@@ -42,15 +45,20 @@ template <int D_, int NW_, int BN_> struct Cfg {
   static constexpr uint32_t dmaStrideV = 1024u;          // source step per V issue
   static_assert(tileBytes % (1024 * NW) == 0, "tile must split into whole DMA issues");
   static_assert(BN % 32 == 0, "KV tile must be whole 32-key MFMA blocks");
+  static_assert(RPW % kRowsPerWave == 0, "a wave owns whole 32-row blocks");
 };
 
-// The two kernels: four waves (128 query rows) with a two- or three-stage
+// The kernels: four waves (128 query rows) with a two- or three-stage
 // register pipeline per wave, for grids too small to fill the chip with
 // 256-row tiles; eight waves (256 rows) in two groups that alternate MFMA
-// and softmax phases (ping-pong) otherwise. The ping-pong kernel uses 128-key
+// and softmax phases (ping-pong); four waves of 64 rows (256 rows). The ping-pong kernel uses 128-key
 // tiles at D=64 so that an MFMA phase (32 MFMAs) balances a softmax phase.
 template <int D> using Cfg4 = Cfg<D, 4, 64>;
 template <int D> using Cfg8 = Cfg<D, 8, (D == 64 ? 128 : 64)>;
+// Four waves of two 32-row blocks each (256 rows): every K/V operand read
+// from LDS feeds both blocks' MFMAs, half the LDS traffic per FLOP of the
+// one-block kernels. 32-key tiles keep both blocks' S and P in registers.
+template <int D> using CfgW2 = Cfg<D, 4, 32, 64>;
 
 // ------------------------------------------------------- work decomposition
 // One work-group per (Q tile, batch*head). Under a causal mask Q tile t needs

@@ -15,8 +15,8 @@
  * FlashAttention way: Q tile resident, K/V tiles streamed, online softmax
  * with running max m and sum l, one normalisation at the end (hotdry.top,
  * "FlashAttention的Triton性能考古学", sections "核心算法回顾" and
- * "FlashAttention v2"), with the running max allowed to lag by 8 in log2
- * units before the accumulator is rescaled (hjcheng0602.cn, "Flash
+ * "FlashAttention v2：循环重构与寄存器积累"), with the running max allowed to
+ * lag by 8 in log2 units before the accumulator is rescaled (hjcheng0602.cn, "Flash
  * Attention CUDA Kernel 优化 ... G6", section "V41: Conditional Scale").
  * The row logsumexp output is this library's own addition; the pages do
  * not define it.
@@ -110,8 +110,10 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse
  *   variant          which kernel runs: 0 = the one fa_fwd picks for this
  *                    shape, 1 = the four-wave kernel (128 query rows per
  *                    work-group), 2 = the eight-wave ping-pong kernel (256
- *                    rows). Every variant computes the same result, to
- *                    rounding; the choice only affects speed.
+ *                    rows), 3 = the four-wave kernel with two 32-row blocks
+ *                    per wave (256 rows, 32-key tiles). Every variant
+ *                    computes the same result, to rounding; the choice only
+ *                    affects speed.
  * It runs separate, instrumented instantiations of the same kernels.
  * Invalid threshold_log2 or variant: FA_ERR_ARG; NULL rescale_events:
  * FA_ERR_NULL; rescale_events not 8-byte aligned: FA_ERR_ALIGN.

@@ -227,7 +227,8 @@ static void check_global(int B, int H, int S, bool causal) {
             }
     }
     for (int wave = 0; wave < C::NW; ++wave) {
-      const int q0w = qt * C::BM + wave * kRowsPerWave;
+      for (int sub = 0; sub < C::RPW / kRowsPerWave; ++sub) {
+      const int q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
       const bool live = q0w < S;
       const int nw = live ? (wave_kv_end(q0w, S, causal) + BN - 1) / BN : 0;
       CHECK(nw <= ntiles, "wave computes a tile the work-group does not load");
@@ -272,6 +273,7 @@ static void check_global(int B, int H, int S, bool causal) {
             CHECK((uint32_t)qrow * 4u >= (uint32_t)S * 4u, "lse past S in range");
           }
         }
+      }
       }
     }
   }
@@ -390,11 +392,52 @@ static void check_pingpong(int ntiles, int nw) {
   CHECK(pp_slots(ntiles) + 1 == nslots, "slot count");
 }
 
+// Replays the four-wave two-block kernel: one group, iteration j issues
+// K(j+2) and V(j+1) (empty ranges past the last tile), reads K(j) and
+// V(j-1), then waits for all but its latest pair and meets the barrier.
+static void check_w2_schedule(int ntiles) {
+  const int NS = kStages;
+  int ktile[3] = {0, ntiles > 1 ? 1 : -1, -1}, vtile[3] = {0, -1, -1};
+  // slot (iteration) after which each stage's latest DMA is waited for
+  int kland[3] = {-1, -1, -1}, vland[3] = {-1, -1, -1};
+  int kread_last[3] = {-1, -1, -1}, vread_last[3] = {-1, -1, -1};
+  int pend_k = -1, pend_v = -1;  // stages of the latest pair, not yet waited for
+  for (int j = 0; j <= ntiles; ++j) {
+    // DMA pair j at the start of iteration j
+    const int sk = (j + 2) % NS, sv = (j + 1) % NS;
+    CHECK(kread_last[sk] < j, "K stage refilled while still read");
+    CHECK(vread_last[sv] < j, "V stage refilled while still read");
+    ktile[sk] = j + 2 < ntiles ? j + 2 : -1;
+    vtile[sv] = j + 1 < ntiles ? j + 1 : -1;
+    kland[sk] = 1 << 30;
+    vland[sv] = 1 << 30;
+    // reads of iteration j
+    if (j < ntiles) {
+      CHECK(ktile[j % NS] == j && kland[j % NS] < j, "K(%d) not resident at iteration %d", j, j);
+      kread_last[j % NS] = j;
+    }
+    if (j >= 1) {
+      CHECK(vtile[(j + 2) % NS] == j - 1 && vland[(j + 2) % NS] < j,
+            "V(%d) not resident at iteration %d", j - 1, j);
+      vread_last[(j + 2) % NS] = j;
+    }
+    // end of iteration: everything but pair j has landed
+    if (pend_k >= 0) kland[pend_k] = j;
+    if (pend_v >= 0) vland[pend_v] = j;
+    pend_k = sk;
+    pend_v = sv;
+  }
+}
+
 int main() {
   check_lds<Cfg4<64>>();
   check_lds<Cfg4<128>>();
   check_lds<Cfg8<64>>();
   check_lds<Cfg8<128>>();
+  check_lds<CfgW2<64>>();
+  check_lds<CfgW2<128>>();
+  for (int ntiles = 1; ntiles <= 40; ++ntiles) check_w2_schedule(ntiles);
+  std::printf("two-block schedule: ntiles 1..40: checked\n");
   for (int ntiles = 1; ntiles <= 12; ++ntiles)
     for (int nw = 0; nw <= ntiles; ++nw) check_pingpong(ntiles, nw);
   std::printf("ping-pong schedule: ntiles 1..12, every wave tile count: checked\n");
@@ -407,6 +450,8 @@ int main() {
       check_global<Cfg4<128>>(s[0], s[1], s[2], causal);
       check_global<Cfg8<64>>(s[0], s[1], s[2], causal);
       check_global<Cfg8<128>>(s[0], s[1], s[2], causal);
+      check_global<CfgW2<64>>(s[0], s[1], s[2], causal);
+      check_global<CfgW2<128>>(s[0], s[1], s[2], causal);
     }
   // full-size shapes (O coverage tracked up to 64M elements)
   check_global<Cfg4<64>>(1, 16, 1024, true);
@@ -415,6 +460,9 @@ int main() {
   check_global<Cfg8<128>>(1, 8, 16384, true);
   check_global<Cfg4<128>>(1, 1, 65536, true);
   check_global<Cfg8<128>>(1, 1, 65536, true);
+  check_global<CfgW2<128>>(2, 16, 8192, true);
+  check_global<CfgW2<64>>(10, 64, 1024, false);
+  check_global<CfgW2<128>>(1, 1, 65536, true);
   if (g_err) {
     std::printf("FAILED with %d errors\n", g_err);
     return 1;

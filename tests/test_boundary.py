@@ -47,8 +47,8 @@ def test_kernel_launch_stubs_are_defined():
         pytest.skip("no nm")
     out = subprocess.run([nm, "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
     stubs = [l for l in out.splitlines() if "device_stub" in l]
-    # 2 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic thresholds)
-    assert len(stubs) == 48
+    # 3 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic thresholds)
+    assert len(stubs) == 72
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
@@ -124,12 +124,12 @@ def test_diag_validation():
     args = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 8, 64, 0, 0.1, None, 0)
     ev = 0x20000000000
     assert fa.fa_fwd_diag(*args, 3, 0, ev, check=False) == ARG
-    assert fa.fa_fwd_diag(*args, 8, 3, ev, check=False) == ARG
+    assert fa.fa_fwd_diag(*args, 8, 4, ev, check=False) == ARG
     assert fa.fa_fwd_diag(*args, 8, -1, ev, check=False) == ARG
     assert fa.fa_fwd_diag(*args, 8, 0, 0, check=False) == NULL
     assert fa.fa_fwd_diag(*args, 0, 2, ev + 4, check=False) == ALIGN
     e = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 0, 64, 0, 0.1, None, 0)
-    for variant in (0, 1, 2):
+    for variant in (0, 1, 2, 3):
         assert fa.fa_fwd_diag(*e, 8, variant, ev, check=False) == OK
 
 

@@ -23,7 +23,7 @@ def _banner(msg):
     print(msg, flush=True)
 
 
-VARIANTS = {"k4": fa.VARIANT_FOUR_WAVE, "pp": fa.VARIANT_PING_PONG}
+VARIANTS = {"k4": fa.VARIANT_FOUR_WAVE, "pp": fa.VARIANT_PING_PONG, "w2": fa.VARIANT_TWO_BLOCK}
 
 
 def _check_full(qb, kb, vb, dtype, causal, scale, tag, variant=None):
@@ -46,7 +46,7 @@ def test_tiny_workload(causal):
     _check_full(*W.make_inputs(w), w.dtype, causal, w.scale, f"tiny causal={causal}")
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2"])
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
@@ -61,7 +61,7 @@ def test_small_shapes_all_rows(S, causal, D, dtype, kernel):
                 f"S={S} D={D} {dtype} causal={causal} kernel={kernel}", VARIANTS[kernel])
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_many_tiles_all_rows(causal, D, kernel):
@@ -81,9 +81,10 @@ def test_kernels_agree(D):
     S, dt = 777, W.F16
     qb, kb, vb = (W.random_bits((2, 2, S, D), dt, 3000 + D + i) for i in range(3))
     res = [_check_full(qb, kb, vb, dt, True, D ** -0.5, f"agree D={D} {k}", VARIANTS[k])
-           for k in ("k4", "pp")]
-    assert np.abs(res[0][0] - res[1][0]).max() <= O_TOL[dt]
-    assert np.abs(res[0][1] - res[1][1]).max() <= LSE_TOL
+           for k in ("k4", "pp", "w2")]
+    for other in res[1:]:
+        assert np.abs(res[0][0] - other[0]).max() <= O_TOL[dt]
+        assert np.abs(res[0][1] - other[1]).max() <= LSE_TOL
 
 
 # full-size workloads, sampled rows (the oracle computes each row on its own)
@@ -205,7 +206,7 @@ def _diag(qb, kb, vb, dtype, causal, scale, thr, variant=0):
     return o_to_f64(o), lse.cpu().numpy().astype(np.float64), int(ev.item())
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_lagging_and_eager_rescale_both_match(D, kernel):
     """Threshold 8 (production) and 0 (eager) both meet tolerance on a steep
@@ -226,10 +227,11 @@ def test_lagging_and_eager_rescale_both_match(D, kernel):
     # the production instantiation of the same kernel gives the same bits
     # (same arithmetic, counter aside)
     o, lse = run(qb, kb, vb, dt, True, w.scale, variant=None)
-    if fa.fa_fwd_tile(D, w.B, w.H, w.S)[0] == (256 if kernel == "pp" else 128):
+    auto_kernel = "pp" if fa.fa_fwd_tile(D, w.B, w.H, w.S)[2] == 512 else "k4"
+    if kernel == auto_kernel:
         np.testing.assert_array_equal(o_to_f64(o), res[8][0])
     # the float64 model of the algorithm, same KV tile size
-    bn = 128 if (kernel == "pp" and D == 64) else 64
+    bn = {"k4": 64, "pp": 128 if D == 64 else 64, "w2": 32}[kernel]
     model = {8: 0, 0: 0}
     for h in range(w.H):
         q, k, v = (W.decode(x[0, h], dt) for x in (qb, kb, vb))
@@ -252,7 +254,7 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_no_writes_outside_outputs(D, kernel):
     """Outputs embedded in guard bands: the kernel writes only O and lse."""
