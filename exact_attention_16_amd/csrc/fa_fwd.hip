@@ -459,13 +459,18 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
     }
     // step j (R = j mod 3): MFMA phase P(j-1).V(j-1) + S(j) = K(j) Q^T, then
     // the softmax phase of S(j). K(j) sits in stage R, V(j-1) in stage R-1.
+    // The MFMA phase runs at raised wave priority, so that on each SIMD the
+    // multiplying wave's MFMAs and LDS reads issue ahead of the other
+    // wave's exponentials whenever both are ready.
     auto step = [&](auto r, int j) {
       constexpr int R = decltype(r)::value;
+      __builtin_amdgcn_s_setprio(1);
       if constexpr (G == 0) dma_pair(r, j);
       __builtin_amdgcn_sched_barrier(0);
       if (j >= 1 && j - 1 < nw) w.pv(p, pick3<(R + 2) % 3>(lv0, lv1, lv2));
       if (j < nw) w.qk(s, pick3<R>(lk0, lk1, lk2));
       end_slot();
+      __builtin_amdgcn_s_setprio(0);
       if constexpr (G == 1) dma_pair(IC<(R + 1) % 3>{}, j + 1);
       __builtin_amdgcn_sched_barrier(0);
       if (j < nw) w.softmax_tile(s, p, j);

@@ -54,7 +54,7 @@ template <int D_, int NW_, int BN_, int RPW_ = kRowsPerWave> struct Cfg {
 // and softmax phases (ping-pong); four waves of 64 rows (256 rows). The ping-pong kernel uses 128-key
 // tiles at D=64 so that an MFMA phase (32 MFMAs) balances a softmax phase.
 template <int D> using Cfg4 = Cfg<D, 4, 64>;
-template <int D> using Cfg8 = Cfg<D, 8, (D == 64 ? 128 : 64)>;
+template <int D> using Cfg8 = Cfg<D, 8, (D == 64 ? 128 : 96)>;
 // Four waves of two 32-row blocks each (256 rows): every K/V operand read
 // from LDS feeds both blocks' MFMAs, half the LDS traffic per FLOP of the
 // one-block kernels. 32-key tiles keep both blocks' S and P in registers.

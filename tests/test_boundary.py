@@ -61,10 +61,10 @@ def test_version_and_strerror():
 
 def test_tile_query():
     # eight-wave kernel once B*H*ceil(S/256) >= 256 work-groups, else four-wave
-    assert fa.fa_fwd_tile(128, 2, 16, 8192) == (256, 64, 512, 2 * 16 * 32)
+    assert fa.fa_fwd_tile(128, 2, 16, 8192) == (256, 96, 512, 2 * 16 * 32)
     assert fa.fa_fwd_tile(64, 10, 64, 1024) == (256, 128, 512, 640 * 4)
     assert fa.fa_fwd_tile(64, 1, 16, 1024) == (128, 64, 256, 16 * 8)
-    assert fa.fa_fwd_tile(128, 1, 64, 1024) == (256, 64, 512, 256)
+    assert fa.fa_fwd_tile(128, 1, 64, 1024) == (256, 96, 512, 256)
     assert fa.fa_fwd_tile(128, 1, 63, 1024) == (128, 64, 256, 63 * 8)
     assert fa.fa_fwd_tile(64, 1, 1, 129)[3] == 2
     with pytest.raises(fa.FaError):

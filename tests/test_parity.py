@@ -231,7 +231,9 @@ def test_lagging_and_eager_rescale_both_match(D, kernel):
     if kernel == auto_kernel:
         np.testing.assert_array_equal(o_to_f64(o), res[8][0])
     # the float64 model of the algorithm, same KV tile size
-    bn = {"k4": 64, "pp": 128 if D == 64 else 64, "w2": 32}[kernel]
+    # KV tile of the forced kernel: the eight-wave kernel's from the tile
+    # query on a grid large enough for fa_fwd to pick it
+    bn = {"k4": 64, "pp": fa.fa_fwd_tile(D, 1, 256, 1024)[1], "w2": 32}[kernel]
     model = {8: 0, 0: 0}
     for h in range(w.H):
         q, k, v = (W.decode(x[0, h], dt) for x in (qb, kb, vb))
