@@ -394,6 +394,7 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   using W = Wave<T, C, CAUSAL, THR, DIAG>;
   constexpr int TB = C::tileBytes;
   constexpr int DPW = C::dmaPerWave;
+  constexpr bool ONE = pp_one_barrier<D>;  // one barrier per step, else two
   static_assert(kStages == 3, "the step below is unrolled over three stages");
   // One array per stage: with the stage fixed at compile time the compiler
   // sees that an LDS read never aliases the DMA in flight into another stage
@@ -446,16 +447,18 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   __builtin_amdgcn_s_waitcnt(0);
   wg_barrier();
 
-  // Group A runs local step j in slots (2j, 2j+1), group B in (2j+1, 2j+2):
-  // B takes slot 0 alone first and A takes the last slot alone at the end,
-  // so both groups pass the same number of barriers. Each group has its own
+  // With two barriers per step group A runs step j in slots (2j, 2j+1),
+  // group B in (2j+1, 2j+2): B takes slot 0 alone first and A takes the last
+  // slot alone at the end, so both groups pass the same number of barriers.
+  // With one, slot j holds A's step j and B's softmax phase of step j-1 and
+  // MFMA phase of step j. Each group has its own
   // copy of the loop, in which every DMA is unconditional: the compiler's
   // count of DMA in flight then matches the constant waits on every path.
   auto run = [&](auto g) {
     constexpr int G = decltype(g)::value;
     if constexpr (G == 1) {
       dma_pair(IC<0>{}, 0);
-      end_slot();
+      if constexpr (!ONE) end_slot();
     }
     // step j (R = j mod 3): MFMA phase P(j-1).V(j-1) + S(j) = K(j) Q^T, then
     // the softmax phase of S(j). K(j) sits in stage R, V(j-1) in stage R-1.
@@ -469,12 +472,20 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
       __builtin_amdgcn_sched_barrier(0);
       if (j >= 1 && j - 1 < nw) w.pv(p, pick3<(R + 2) % 3>(lv0, lv1, lv2));
       if (j < nw) w.qk(s, pick3<R>(lk0, lk1, lk2));
-      end_slot();
+      if constexpr (ONE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (G == 1) end_slot();
+      } else {
+        end_slot();
+      }
       __builtin_amdgcn_s_setprio(0);
-      if constexpr (G == 1) dma_pair(IC<(R + 1) % 3>{}, j + 1);
       __builtin_amdgcn_sched_barrier(0);
       if (j < nw) w.softmax_tile(s, p, j);
-      end_slot();
+      // group B's DMA share goes after its softmax work, clear of group A's
+      // issues at the start of the slot
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (G == 1) dma_pair(IC<(R + 1) % 3>{}, j + 1);
+      if constexpr (!ONE || G == 0) end_slot();
     };
     for (int j = 0;; j += 3) {
       step(IC<0>{}, j);
@@ -484,7 +495,7 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
       step(IC<2>{}, j + 2);
       if (j + 3 > ntiles) break;
     }
-    if constexpr (G == 0) end_slot();
+    if constexpr (G == 0 && !ONE) end_slot();
   };
   if (grp == 0) run(IC<0>{});
   else run(IC<1>{});

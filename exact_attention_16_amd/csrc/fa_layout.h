@@ -214,17 +214,34 @@ template <int D> FA_HD uint32_t o_frag_off(int qrow, int jd, int g, int hh) {
 
 // ------------------------------------- ping-pong schedule (eight waves)
 // Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs one each (wave
-// w and w+4 land on the same SIMD). Time is divided in slots separated by
-// work-group barriers; slot t of a wave runs its local phase t - group:
-// even phase 2j = MFMA phase (O += P(j-1) V(j-1), S(j) = K(j) Q^T), odd
-// phase 2j+1 = softmax phase of S(j). So in every slot one wave of each SIMD
+// w and w+4 land on the same SIMD). Each wave runs steps j = 0..ntiles: an
+// MFMA phase (O += P(j-1) V(j-1), S(j) = K(j) Q^T), then the softmax phase of
+// S(j). Group B runs half a step behind group A, so that on each SIMD one wave
 // multiplies while the other exponentiates. KV tile t lives in LDS stage
-// t mod kStages for both K and V. In even slot 2i each wave issues its share
-// of K(i+2) and V(i+1); at the end of odd slot 2i+1 it waits for all but its
-// latest share, so everything issued by slot 2i-2 has landed -- K(j) before
-// slot 2j, V(j) before slot 2j+2. A stage is refilled only after both groups
-// have read it: K(j-3) is last read in slot 2j-5, V(j-3) in slot 2j-3.
+// t mod kStages for both K and V. DMA pair i carries K(i+2) and V(i+1); each
+// wave issues its share of it in step i (group A before its MFMA phase, group
+// B after the softmax phase of step i-1). Work-group barriers divide time in
+// slots, and at the end of every slot each wave waits for all its DMA but the
+// latest pair. Two forms:
+//  * two barriers per step: slot t of a wave runs its phase t - group (phase
+//    2j: MFMA phase of step j, 2j+1: its softmax phase), so the phases of the
+//    two groups are pinned to each other. Pair i is issued in slot 2i and has
+//    landed by the end of slot 2i+2: K(j) and V(j-1), both of pair j-2, are
+//    in place from slot 2j-1 on. Pair i overwrites K(i-1) and V(i-2), both
+//    last read (by group B) in slot 2i-1.
+//  * one barrier per step: slot e holds group A's step e and group B's
+//    softmax phase of step e-1 and MFMA phase of step e; within a slot the
+//    phases alternate without being pinned. Pair i is issued in slot i and
+//    has landed by the end of slot i+1: K(j) and V(j-1) are in place from
+//    slot j on. Pair i overwrites K(i-1) and V(i-2), last read in slot i-1.
+// At D = 128 the second barrier costs more than the drift it prevents; at
+// D = 64 the softmax phase is as long as the MFMA phase and the pinned form
+// keeps the two groups from exponentiating at the same time.
 constexpr int kStages = 3;
-FA_HD int pp_slots(int ntiles) { return 2 * ntiles + 2; }
+template <int D> constexpr bool pp_one_barrier = (D == 128);
+// barriers after the prologue's
+FA_HD int pp_slots(int ntiles, bool one_barrier) {
+  return one_barrier ? ntiles + 1 : 2 * ntiles + 3;
+}
 
 }  // namespace fa

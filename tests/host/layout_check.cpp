@@ -299,8 +299,9 @@ struct Stage {
 
 // Replays the slots of both groups of the eight-wave kernel for a work-group
 // with `ntiles` KV tiles and waves that compute `nw` of them, mirroring the
-// kernel's code order, and checks every read and every overwrite.
-static void check_pingpong(int ntiles, int nw) {
+// kernel's code order (with one or two barriers per step), and checks every
+// read and every overwrite.
+static void check_pingpong(int ntiles, int nw, bool one_barrier) {
   const int NS = kStages;
   Stage kst[3], vst[3];
   // pending DMA per group: (array, stage index) of each share of the latest
@@ -365,31 +366,53 @@ static void check_pingpong(int ntiles, int nw) {
     issue(g, &vst[2], -1, -1, -1);
     wait_all(g, -1);
   }
-  // Both groups advance slot by slot; the slot numbers of each group's code
-  // follow the kernel: A runs step j in (2j, 2j+1), B in (2j+1, 2j+2).
-  const int nslots = 2 * ntiles + 3;
-  for (int t = 0; t < nslots; ++t) {
-    for (int g = 0; g < 2; ++g) {
-      const int local = t - g;  // B's slot 0 is its lone DMA slot
-      if (g == 1 && t == 0) {
-        dma_pair(1, 0, t);
-      } else if (g == 0 && t == nslots - 1) {
-        // A's lone last slot
-      } else {
-        const int j = local / 2;
-        if (local % 2 == 0) {  // MFMA phase of step j
-          if (g == 0) dma_pair(0, j, t);
-          if (j >= 1 && j - 1 < nw) read(&vst[(j + 2) % NS], j - 1, t);
-          if (j < nw) read(&kst[j % NS], j, t);
-        } else {  // softmax phase of step j
-          if (g == 1) dma_pair(1, j + 1, t);
+  auto step_reads = [&](int j, int t) {
+    if (j >= 1 && j - 1 < nw) read(&vst[(j + 2) % NS], j - 1, t);
+    if (j < nw) read(&kst[j % NS], j, t);
+  };
+  int nslots;
+  if (one_barrier) {
+    // slot t: A issues pair t, then its MFMA phase of step t; B runs its
+    // softmax phase of step t-1 (no LDS access), issues pair t (pair 0 before
+    // its loop), then its MFMA phase of step t.
+    nslots = ntiles + 1;
+    for (int t = 0; t < nslots; ++t) {
+      for (int g = 0; g < 2; ++g) {
+        dma_pair(g, t, t);
+        step_reads(t, t);
+      }
+      for (int g = 0; g < 2; ++g) wait_all_but_latest(g, t);
+    }
+  } else {
+    // Both groups advance slot by slot; the slot numbers of each group's
+    // code follow the kernel: A runs step j in (2j, 2j+1), B in (2j+1, 2j+2).
+    nslots = 2 * ntiles + 3;
+    for (int t = 0; t < nslots; ++t) {
+      for (int g = 0; g < 2; ++g) {
+        const int local = t - g;  // B's slot 0 is its lone DMA slot
+        if (g == 1 && t == 0) {
+          dma_pair(1, 0, t);
+        } else if (g == 0 && t == nslots - 1) {
+          // A's lone last slot
+        } else {
+          const int j = local / 2;
+          if (local % 2 == 0) {  // MFMA phase of step j
+            if (g == 0) dma_pair(0, j, t);
+            step_reads(j, t);
+          } else {  // softmax phase of step j
+            if (g == 1) dma_pair(1, j + 1, t);
+          }
         }
       }
+      for (int g = 0; g < 2; ++g) wait_all_but_latest(g, t);
     }
-    for (int g = 0; g < 2; ++g) wait_all_but_latest(g, t);
   }
   for (int g = 0; g < 2; ++g) wait_all(g, nslots);
-  CHECK(pp_slots(ntiles) + 1 == nslots, "slot count");
+  CHECK(pp_slots(ntiles, one_barrier) == nslots, "slot count");
+  // every tile was read by both groups
+  int nread = 0;
+  for (auto& kv : reads) nread += (int)kv.second.size();
+  CHECK(nread == 2 * 2 * nw, "read count %d for %d wave tiles", nread, nw);
 }
 
 // Replays the four-wave two-block kernel: one group, iteration j issues
@@ -439,8 +462,10 @@ int main() {
   for (int ntiles = 1; ntiles <= 40; ++ntiles) check_w2_schedule(ntiles);
   std::printf("two-block schedule: ntiles 1..40: checked\n");
   for (int ntiles = 1; ntiles <= 12; ++ntiles)
-    for (int nw = 0; nw <= ntiles; ++nw) check_pingpong(ntiles, nw);
-  std::printf("ping-pong schedule: ntiles 1..12, every wave tile count: checked\n");
+    for (int nw = 0; nw <= ntiles; ++nw)
+      for (int one = 0; one < 2; ++one) check_pingpong(ntiles, nw, one != 0);
+  CHECK(pp_one_barrier<128> && !pp_one_barrier<64>, "schedule form per head size");
+  std::printf("ping-pong schedules (one and two barriers per step): ntiles 1..12, every wave tile count: checked\n");
   const int shapes[][3] = {{1, 1, 1}, {1, 1, 7}, {1, 1, 64}, {1, 1, 127}, {1, 1, 128},
                            {1, 1, 129}, {1, 2, 200}, {2, 3, 255}, {2, 3, 300}, {1, 1, 1000},
                            {1, 16, 1024}, {1, 1, 4097}};
