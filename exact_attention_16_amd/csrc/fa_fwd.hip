@@ -102,10 +102,15 @@ template <> struct Ops<_Float16> {
 // the same query row): v_permlane32_swap exchanges the upper half-wave of
 // one copy with the lower half-wave of the other, so the two results hold
 // both values in every lane and a symmetric op combines them.
+// The maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950):
+// fmaxf's NaN-ignoring form costs an extra quieting op per operand that
+// does not come from plain arithmetic (MFMA results, lane exchanges). A NaN
+// score makes its row NaN through the exponential either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max_xor32(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  return vmax(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 __device__ __forceinline__ float sum_xor32(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -162,6 +167,20 @@ __device__ __forceinline__ void interleave() {
     __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, V2, 0);
+  }
+}
+
+// Scheduling pattern for one MFMA loop: DS0 LDS reads up front, then N
+// times {one MFMA, DS LDS reads}, so that each MFMA's operands are read
+// several MFMAs ahead of it. (Left to itself the scheduler reads them just
+// before their MFMA, which then waits for the LDS round trip.)
+template <int DS0, int N, int DS>
+__device__ __forceinline__ void read_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
   }
 }
 
@@ -301,9 +320,9 @@ struct Wave {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
     mx = max_xor32(mx);
-    const float cand = fmaxf(b, mx * c);
+    const float cand = vmax(b, mx * c);
     const bool rebase = cand > b + (float)THR;
     const float hist = rebase ? __builtin_amdgcn_exp2f(b - cand) : 1.f;  // 0 on the first tile
     b = rebase ? cand : b;
@@ -313,7 +332,7 @@ struct Wave {
   // p = 2^(s*c - b), row sum of the unrounded p, P packed for the P.V MFMA
   __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[NKB], u32x4 (&p)[NKC]) {
     const float nb = (b == -INFINITY) ? 0.f : -b;  // fully hidden row: p = 0
-    float ls = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four sum chains, so no add waits on the one before
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -322,12 +341,12 @@ struct Wave {
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           e[x] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + x], c, nb));
-          ls += e[x];
+          ls[x & 3] += e[x];
         }
         p[2 * kb + g] = (u32x4){Ops<T>::pack2(e[0], e[1]), Ops<T>::pack2(e[2], e[3]),
                                 Ops<T>::pack2(e[4], e[5]), Ops<T>::pack2(e[6], e[7])};
       }
-    lsum += ls;
+    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   }
   // rare path: some row of the wave moved its base -> rescale O
   __device__ __forceinline__ void rescale(int j, float hist) {
@@ -398,19 +417,23 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   static_assert(kStages == 3, "the step below is unrolled over three stages");
   // One array per stage: with the stage fixed at compile time the compiler
   // sees that an LDS read never aliases the DMA in flight into another stage
-  // and inserts no wait for it.
-  __shared__ __attribute__((aligned(1024))) char ks0[TB];
-  __shared__ __attribute__((aligned(1024))) char ks1[TB];
-  __shared__ __attribute__((aligned(1024))) char ks2[TB];
-  __shared__ __attribute__((aligned(1024))) char vs0[TB];
-  __shared__ __attribute__((aligned(1024))) char vs1[TB];
-  __shared__ __attribute__((aligned(1024))) char vs2[TB];
-  lds_char* const lk0 = (lds_char*)ks0;
-  lds_char* const lk1 = (lds_char*)ks1;
-  lds_char* const lk2 = (lds_char*)ks2;
-  lds_char* const lv0 = (lds_char*)vs0;
-  lds_char* const lv1 = (lds_char*)vs1;
-  lds_char* const lv2 = (lds_char*)vs2;
+  // and inserts no wait for it. The compiler lays the arrays out in name
+  // order; the V stages are named to come first, so that their transposed
+  // reads (two per P.V MFMA, the part of the MFMA phase with the most
+  // instructions per MFMA) mostly fit the 16-bit offset field of the LDS
+  // instruction and need no address arithmetic. This affects speed only.
+  __shared__ __attribute__((aligned(1024))) char a_vstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage1[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage2[TB];
+  __shared__ __attribute__((aligned(1024))) char b_kstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char b_kstage1[TB];
+  __shared__ __attribute__((aligned(1024))) char b_kstage2[TB];
+  lds_char* const lk0 = (lds_char*)b_kstage0;
+  lds_char* const lk1 = (lds_char*)b_kstage1;
+  lds_char* const lk2 = (lds_char*)b_kstage2;
+  lds_char* const lv0 = (lds_char*)a_vstage0;
+  lds_char* const lv1 = (lds_char*)a_vstage1;
+  lds_char* const lv2 = (lds_char*)a_vstage2;
 
   W w;
   w.init(Q, K, V, BH, S, nqt, c);
@@ -470,8 +493,14 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
       __builtin_amdgcn_s_setprio(1);
       if constexpr (G == 0) dma_pair(r, j);
       __builtin_amdgcn_sched_barrier(0);
-      if (j >= 1 && j - 1 < nw) w.pv(p, pick3<(R + 2) % 3>(lv0, lv1, lv2));
-      if (j < nw) w.qk(s, pick3<R>(lk0, lk1, lk2));
+      if (j >= 1 && j - 1 < nw) {
+        w.pv(p, pick3<(R + 2) % 3>(lv0, lv1, lv2));
+        read_ahead<8, W::NKC * W::NDB, 2>();  // two reads per MFMA, four MFMAs ahead
+      }
+      if (j < nw) {
+        w.qk(s, pick3<R>(lk0, lk1, lk2));
+        read_ahead<4, W::NDC * W::NKB, 1>();  // one read per MFMA, four MFMAs ahead
+      }
       if constexpr (ONE) {
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (G == 1) end_slot();
@@ -528,18 +557,19 @@ fa_fwd_w2(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   constexpr int NKB = W::NKB, NKC = W::NKC, NDC = W::NDC, NDB = W::NDB;
   constexpr uint32_t RB = C::rowBytes;
   static_assert(kStages == 3, "the step below is unrolled over three stages");
-  __shared__ __attribute__((aligned(1024))) char ks0[TB];
-  __shared__ __attribute__((aligned(1024))) char ks1[TB];
-  __shared__ __attribute__((aligned(1024))) char ks2[TB];
-  __shared__ __attribute__((aligned(1024))) char vs0[TB];
-  __shared__ __attribute__((aligned(1024))) char vs1[TB];
-  __shared__ __attribute__((aligned(1024))) char vs2[TB];
-  lds_char* const lk0 = (lds_char*)ks0;
-  lds_char* const lk1 = (lds_char*)ks1;
-  lds_char* const lk2 = (lds_char*)ks2;
-  lds_char* const lv0 = (lds_char*)vs0;
-  lds_char* const lv1 = (lds_char*)vs1;
-  lds_char* const lv2 = (lds_char*)vs2;
+  // one array per stage, V stages first in name order (as in fa_fwd_pp)
+  __shared__ __attribute__((aligned(1024))) char b_kstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char b_kstage1[TB];
+  __shared__ __attribute__((aligned(1024))) char b_kstage2[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage1[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage2[TB];
+  lds_char* const lk0 = (lds_char*)b_kstage0;
+  lds_char* const lk1 = (lds_char*)b_kstage1;
+  lds_char* const lk2 = (lds_char*)b_kstage2;
+  lds_char* const lv0 = (lds_char*)a_vstage0;
+  lds_char* const lv1 = (lds_char*)a_vstage1;
+  lds_char* const lv2 = (lds_char*)a_vstage2;
 
   W wa, wb;
   wa.init(Q, K, V, BH, S, nqt, c, 0);
@@ -685,14 +715,15 @@ fa_fwd_k4(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   constexpr bool P3 = Pipe<D>::three;
   constexpr int NKB = W::NKB, NKC = W::NKC;
   constexpr int TB = C::tileBytes;
-  __shared__ __attribute__((aligned(1024))) char ks0[TB];
-  __shared__ __attribute__((aligned(1024))) char ks1[TB];
-  __shared__ __attribute__((aligned(1024))) char vs0[TB];
-  __shared__ __attribute__((aligned(1024))) char vs1[TB];
-  lds_char* const lk0 = (lds_char*)ks0;
-  lds_char* const lk1 = (lds_char*)ks1;
-  lds_char* const lv0 = (lds_char*)vs0;
-  lds_char* const lv1 = (lds_char*)vs1;
+  // one array per stage, V stages first in name order (as in fa_fwd_pp)
+  __shared__ __attribute__((aligned(1024))) char b_kstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char b_kstage1[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage1[TB];
+  lds_char* const lk0 = (lds_char*)b_kstage0;
+  lds_char* const lk1 = (lds_char*)b_kstage1;
+  lds_char* const lv0 = (lds_char*)a_vstage0;
+  lds_char* const lv1 = (lds_char*)a_vstage1;
 
   W w;
   w.init(Q, K, V, BH, S, nqt, c);
@@ -721,7 +752,7 @@ fa_fwd_k4(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (nw > 0) w.qk(sA, lk0);
-  __syncthreads();  // ks0 is refilled with K(2) in iteration 0
+  __syncthreads();  // b_kstage0 is refilled with K(2) in iteration 0
 
   // ---- iteration j (PH = j % 2). DMA first (K(j+2); V(j) with three stages,
   // V(j+1) with two). A wave that still has tile j then computes; at its
