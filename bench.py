@@ -13,6 +13,10 @@ Default workload: B=2, H=16, S=8192, D=128, bf16, causal (the long-context
 configuration the metric is quoted on). FLOPs follow the metric:
 4*B*H*S^2*D, halved when causal.
 
+--varlen times the variable-length entry point instead, on a packed batch of
+16 causal sequences with seeded lengths in [256, 8192] (H=16, D=128, bf16),
+and prints its own JSON line; FLOPs then sum the metric over the sequences.
+
 Extra modes (used to take profiles): --calibrate-copy runs plain device
 copies of a known size first (for scaling HBM byte counters);
 --no-cpu-baseline skips the oracle leg; --write-traffic FETCH_CSV WRITE_CSV
@@ -187,6 +191,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run plain 1 GiB device copies first (counter scaling)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time fa_fwd_varlen on the packed variable-length batch")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic file from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
@@ -203,6 +209,8 @@ def main(argv=None) -> int:
     import torch
     import exact_attention_16_amd as fa
 
+    if args.varlen:
+        return bench_varlen(args, torch, fa)
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     fa.load()  # fails loudly if the HIP library is not built
@@ -294,6 +302,62 @@ def main(argv=None) -> int:
         "wall_s": wall,
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_varlen(args, torch, fa) -> int:
+    """Time fa_fwd_varlen on the packed variable-length batch; one JSON line."""
+    w = W.VARLEN
+    dev = torch.device("cuda:0")
+    fa.load()
+    cu, qb, kb, vb = W.make_varlen_inputs(w)
+    L = w.lengths()
+    total = int(cu[-1])
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+               for x in (qb, kb, vb))
+    cu_d = torch.from_numpy(cu).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.H, total), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    st = [w.D, w.H * w.D] * 4 + [total]
+
+    def step():
+        fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         cu_d.data_ptr(), cu_d.data_ptr(), w.B, w.H, int(L.max()), int(L.max()),
+                         total, total, w.D, int(w.causal), w.scale, stream.cuda_stream,
+                         W.DTYPE_CODE[w.dtype], st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    assert bool(torch.isfinite(lse).all()), "non-finite output"
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    print(f"Average Time Per Step:     {ms:.4f} ms\n"
+          f"Compute Performance:       {tflops:.2f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of "
+          f"{PEAK_TFLOPS} peak)", file=sys.stderr, flush=True)
+    out = {
+        "metric": "varlen attention fwd TFLOPS (sum over sequences of H·L²·D·4, causal halved)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic: seeded N(0,1) Q/K/V, "
+        "seeded uniform lengths",
+        "config": {"workload": f"varlen: {w.B} causal sequences, lengths uniform in "
+                               f"[{w.lo}, {w.hi}] (seed {w.seed}; {total} tokens), H={w.H} "
+                               f"D={w.D} {w.dtype}, packed [total, H, D]",
+                   "lengths": [int(x) for x in L], "parallelism": "single GPU"},
+        "pct_of_peak": 100 * tflops / PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_TFLOPS, "traffic": None,
+                     "flops_per_launch": w.flops(), "avg_launch_ms": ms},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -29,7 +29,7 @@ VARIANT_TWO_BLOCK = 3
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_DIM", -3: "FA_ERR_UNSUPPORTED",
     -4: "FA_ERR_ALIGN", -5: "FA_ERR_SCALE", -6: "FA_ERR_ALIAS", -7: "FA_ERR_HIP",
-    -8: "FA_ERR_ARG",
+    -8: "FA_ERR_ARG", -9: "FA_ERR_LAYOUT",
 }
 
 # exported symbol -> (restype, argtypes)
@@ -42,6 +42,8 @@ SIGNATURES = {
     "fa_fwd_f16": (_I, _FWD_ARGS),
     "fa_fwd_bf16": (_I, _FWD_ARGS),
     "fa_fwd_diag": (_I, _FWD_ARGS + [_I, _I, _I, _P]),
+    "fa_fwd_strided": (_I, [_P] * 5 + [_I] * 6 + [_F, _P, _I, _P]),
+    "fa_fwd_varlen": (_I, [_P] * 7 + [_I] * 8 + [_F, _P, _I, _P]),
     "fa_fwd_tile": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
                          ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_longlong)]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
@@ -103,6 +105,30 @@ def fa_fwd_diag(q, k, v, o, lse, B, H, S, D, causal, scale, stream, dtype,
     return _check(st, "fa_fwd_diag") if check else st
 
 
+def _strides(values, n):
+    if len(values) != n:
+        raise ValueError(f"expected {n} strides, got {len(values)}")
+    return (ctypes.c_longlong * n)(*[int(x) for x in values])
+
+
+def fa_fwd_strided(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, stream, dtype, strides,
+                   check=True):
+    """strides: 14 element strides, q/k/v/o (batch, head, row) then lse (batch, head)."""
+    st = load().fa_fwd_strided(q, k, v, o, lse, B, H, Sq, Sk, D, int(causal), scale, stream,
+                               dtype, _strides(strides, 14))
+    return _check(st, "fa_fwd_strided") if check else st
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q,
+                  max_seqlen_k, total_q, total_k, D, causal, scale, stream, dtype, strides,
+                  check=True):
+    """strides: 9 element strides, q/k/v/o (head, row) then lse (head)."""
+    st = load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q,
+                              max_seqlen_k, total_q, total_k, D, int(causal), scale, stream,
+                              dtype, _strides(strides, 9))
+    return _check(st, "fa_fwd_varlen") if check else st
+
+
 def fa_fwd_tile(D, B=0, H=0, S=0):
     """(block_m, block_n, threads, work_groups) for head dim D."""
     bm, bn, th = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
@@ -131,32 +157,115 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def attention(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None,
-              stream=None):
-    """Attention forward on torch device tensors of shape [B, H, S, D].
-
-    Returns (o, lse). `out`/`lse` may be given to avoid allocation. The kernel
-    is enqueued on `stream` (default: torch's current stream) and the call
-    returns without synchronising.
-    """
-    import torch
+def _check_inputs(q, k, v, dims):
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
-    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
-        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    if not (q.dim() == k.dim() == v.dim() == dims):
+        raise ValueError(f"q, k, v must have {dims} dimensions")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
-    B, H, S, D = q.shape
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    for t in (q, k, v):
+        if t.stride(-1) != 1:
+            raise ValueError("the last dimension (D) must be contiguous")
+
+
+def attention(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None,
+              stream=None, layout: str = "bhsd"):
+    """Attention forward on torch device tensors.
+
+    layout "bhsd": q [B, H, Sq, D], k and v [B, H, Sk, D]; "bshd": q
+    [B, Sq, H, D], k and v [B, Sk, H, D]. Any strides with a contiguous last
+    dimension (views, slices, transposes); a causal mask with Sq != Sk is
+    aligned bottom-right. Returns (o, lse): o in q's shape and layout (a new
+    contiguous tensor unless `out` is given), lse [B, H, Sq] float32. The
+    kernel is enqueued on `stream` (default: torch's current stream) and the
+    call returns without synchronising.
+    """
+    import torch
+    _check_inputs(q, k, v, 4)
+    if layout == "bhsd":
+        B, H, Sq, D = q.shape
+        Sk = k.shape[2]
+        if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+            raise ValueError("k, v must be [B, H, Sk, D] with q's B, H, D")
+        perm = (0, 1, 2)
+    elif layout == "bshd":
+        B, Sq, H, D = q.shape
+        Sk = k.shape[1]
+        if k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+            raise ValueError("k, v must be [B, Sk, H, D] with q's B, H, D")
+        perm = (0, 2, 1)
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
     if scale is None:
         scale = D ** -0.5
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-           B, H, S, D, causal, float(scale), stream.cuda_stream, _dtype_code(q))
+    dense = (layout == "bhsd" and Sq == Sk and q.is_contiguous() and k.is_contiguous()
+             and v.is_contiguous() and out.is_contiguous() and lse.is_contiguous()
+             and out.shape == q.shape and lse.shape == (B, H, Sq))
+    if dense:
+        fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+               B, H, Sq, D, causal, float(scale), stream.cuda_stream, _dtype_code(q))
+        return out, lse
+    strides = []
+    for t in (q, k, v, out):
+        strides += [t.stride(i) for i in perm]
+    if lse.dim() != 3 or lse.stride(2) != 1:
+        raise ValueError("lse must be [B, H, Sq] with contiguous rows")
+    strides += [lse.stride(0), lse.stride(1)]
+    fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                   B, H, Sq, Sk, D, causal, float(scale), stream.cuda_stream, _dtype_code(q),
+                   strides)
+    return out, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                     max_seqlen_k: int, causal: bool, scale: float | None = None, out=None,
+                     lse=None, stream=None):
+    """Attention forward over sequences of different lengths packed along a token axis.
+
+    q [total_q, H, D], k and v [total_k, H, D] (any strides with a
+    contiguous last dimension); cu_seqlens_q / cu_seqlens_k: int32 device
+    tensors of B+1 non-decreasing token offsets (sequence b owns query tokens
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1, key tokens likewise). Returns
+    (o, lse): o [total_q, H, D], lse [H, total_q] float32. Causal masks are
+    aligned bottom-right within each sequence.
+    """
+    import torch
+    _check_inputs(q, k, v, 3)
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    if k.shape[1] != H or k.shape[2] != D:
+        raise ValueError("k, v must be [total_k, H, D] with q's H and D")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if not cu.is_cuda or cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32 device tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 offsets")
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((total_q, H, D), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if lse.dim() != 2 or lse.stride(1) != 1:
+        raise ValueError("lse must be [H, total_q] with contiguous rows")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    strides = []
+    for t in (q, k, v, out):
+        strides += [t.stride(1), t.stride(0)]
+    strides += [lse.stride(0)]
+    fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                  cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, int(max_seqlen_q),
+                  int(max_seqlen_k), total_q, total_k, D, causal, float(scale),
+                  stream.cuda_stream, _dtype_code(q), strides)
     return out, lse

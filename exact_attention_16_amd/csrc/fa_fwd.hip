@@ -184,6 +184,33 @@ __device__ __forceinline__ void read_ahead() {
   }
 }
 
+// What one launch computes, passed to the kernels by value. Strides are in
+// elements; a row is D contiguous elements. Without per-sequence offsets
+// (cuq == nullptr) sequence b, head h has Sq query rows starting at
+// q + b*qb + h*qh (row stride qs) and Sk key rows in k and v likewise; o has
+// q's row count and lse is Sq floats at lse + b*lb + h*lh. With offsets,
+// sequence b's query rows are token rows cuq[b] .. cuq[b+1]-1 (so its rows
+// start at q + cuq[b]*qs + h*qh, lse + h*lh + cuq[b]) and its key rows are
+// token rows cuk[b] .. cuk[b+1]-1; the kernel clamps both ranges to the
+// totq / totk token rows the tensors hold and the lengths to Sq / Sk.
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os, lb, lh;
+  const int* cuq;
+  const int* cuk;
+  int totq, totk;
+  int B, H, Sq, Sk;
+  int nqt;  // query tiles per (sequence, head) for the kernel's block of rows
+  float c;  // scale * log2(e)
+  unsigned long long* events;
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
 // One wave's share of a work-group: its query rows, accumulators and the
 // per-tile operations on them.
 template <typename T, class C, bool CAUSAL, int THR, bool DIAG>
@@ -197,87 +224,122 @@ struct Wave {
   static constexpr int DPW = C::dmaPerWave;
   static constexpr uint32_t RB = C::rowBytes;
 
-  int lane, wave, hh, S, q0w, qrow, qt, bh;
-  float c;  // scale * log2(e)
-  const T* Kh;
-  const T* Vh;
+  int lane, wave, hh, q0w, qrow, qt;
+  int Lq, Lk, off;  // this sequence's query and key rows; off = Lk - Lq (causal alignment)
+  float c;          // scale * log2(e)
+  const char* Kh;   // row 0 of this (sequence, head) in k, v, o, lse
+  const char* Vh;
+  char* Oh;
+  float* Lh;
+  uint32_t rsk, rsv, rso;  // row strides in bytes
+  uint32_t dsk, dsv;       // source bytes between successive DMA issues
   uint32_t koff0, voff0, kdo0, vdo0;
   u32x4 qf[NDC];
   f32x16 o[NDB];
   float b, lsum;
   unsigned n_events;
 
+  // Sets up this wave's rows of the work-group's query tile; false when the
+  // tile lies wholly past its sequence's end (the same for every wave of the
+  // work-group, which then returns before any DMA or barrier).
   // sub: which 32-row block of the wave's C::RPW rows this object holds
-  __device__ __forceinline__ void init(const T* Q, const T* K, const T* V, int BH, int S_, int nqt,
-                                       float c_, int sub = 0) {
+  __device__ __forceinline__ bool init(const Problem& P, int sub = 0) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hh = lane >> 5;
-    S = S_;
-    c = c_;
-    block_to_tile(blockIdx.x, BH, nqt, CAUSAL, &qt, &bh);
-    const size_t head = (size_t)bh * (size_t)S * D;
-    Kh = K + head;
-    Vh = V + head;
+    c = P.c;
+    int bh;
+    block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh);
+    const int bb = bh / P.H, h = bh - bb * P.H;
+    long long q0, k0, v0, o0, l0;  // element offsets of row 0
+    if (P.cuq) {
+      const int sq = clampi(P.cuq[bb], 0, P.totq), eq = clampi(P.cuq[bb + 1], sq, P.totq);
+      const int sk = clampi(P.cuk[bb], 0, P.totk), ek = clampi(P.cuk[bb + 1], sk, P.totk);
+      Lq = min(eq - sq, P.Sq);
+      Lk = min(ek - sk, P.Sk);
+      q0 = sq * P.qs + h * P.qh;
+      k0 = sk * P.ks + h * P.kh;
+      v0 = sk * P.vs + h * P.vh;
+      o0 = sq * P.os + h * P.oh;
+      l0 = h * P.lh + sq;
+    } else {
+      Lq = P.Sq;
+      Lk = P.Sk;
+      q0 = bb * P.qb + h * P.qh;
+      k0 = bb * P.kb + h * P.kh;
+      v0 = bb * P.vb + h * P.vh;
+      o0 = bb * P.ob + h * P.oh;
+      l0 = bb * P.lb + h * P.lh;
+    }
+    if (qt * C::BM >= Lq) return false;
+    off = Lk - Lq;
+    Kh = (const char*)P.k + k0 * 2;
+    Vh = (const char*)P.v + v0 * 2;
+    Oh = (char*)P.o + o0 * 2;
+    Lh = P.lse + l0;
+    rsk = (uint32_t)P.ks * 2u;
+    rsv = (uint32_t)P.vs * 2u;
+    rso = (uint32_t)P.os * 2u;
+    dsk = (uint32_t)C::dmaRowsK * rsk;
+    dsv = (uint32_t)C::dmaRowsV * rsv;
     q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
     qrow = q0w + (lane & 31);
-    // Q operand fragments (rows past S read as zeros)
-    const auto rq = FA_RSRC(Q + head, (uint32_t)S * RB);
+    // Q operand fragments (rows past Lq read as zeros)
+    const uint32_t rsq = (uint32_t)P.qs * 2u;
+    const auto rq = FA_RSRC((const char*)P.q + q0 * 2, (uint32_t)Lq * rsq);
 #pragma unroll
     for (int j = 0; j < NDC; ++j)
-      qf[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_frag_off<D>(qrow, j, hh), 0, 0);
+      qf[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_frag_off<D>(qrow, j, hh, rsq), 0, 0);
     // per-lane LDS / DMA base offsets; the rest are XOR / immediate offsets
     koff0 = k_read_off<D>(0, 0, lane);
     voff0 = v_tr_off<D>(0, 0, 0, lane);
-    kdo0 = dma_src_k<C>(wave, 0, lane);
-    vdo0 = dma_src_v<C>(wave, 0, lane);
+    kdo0 = dma_src_k<C>(wave, 0, lane, rsk);
+    vdo0 = dma_src_v<C>(wave, 0, lane, rsv);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) o[j] = (f32x16){};
     b = -INFINITY;  // running base, log2 units (lags the true max by <= THR)
     lsum = 0.f;     // this lane's partial row sum (its k-half of the keys)
     n_events = 0;
+    return true;
   }
 
   // KV tiles this wave computes (0 for a wave wholly past the end), and the
   // work-group's KV tile count.
   __device__ __forceinline__ int wave_tiles() const {
-    return q0w < S ? (wave_kv_end(q0w, S, CAUSAL) + BN - 1) / BN : 0;
+    return q0w < Lq ? (wave_kv_end(q0w, Lq, Lk, CAUSAL) + BN - 1) / BN : 0;
   }
   __device__ __forceinline__ int group_tiles() const {
-    return (tile_kv_end(qt, S, CAUSAL, C::BM) + BN - 1) / BN;
+    return (tile_kv_end(qt, Lq, Lk, CAUSAL, C::BM) + BN - 1) / BN;
   }
 
-  // Leading KV tiles that need no index compares for these rows: tiles
-  // before the one holding key q0w (causal) and before the ragged end.
+  // Leading KV tiles that need no index compares for these rows
   __device__ __forceinline__ int unmasked_tiles() const {
-    const int r = S / BN;
-    const int d = q0w / BN;
-    return CAUSAL ? (d < r ? d : r) : r;
+    return fa::unmasked_tiles(q0w, Lq, Lk, CAUSAL, BN);
   }
 
   // this wave's share of the DMA of K or V tile t into an LDS stage; a tile
   // at or past `limit` is an empty range (the DMA then writes zeros)
   __device__ __forceinline__ void dma_k(lds_char* dst, int t, int limit = 0x7fffffff) const {
     const int kv0 = t * BN;
-    const uint32_t bytes = t < limit ? (uint32_t)(S - kv0) * RB : 0u;
-    const auto r = FA_RSRC(Kh + (size_t)kv0 * D, bytes);
+    const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsk : 0u;
+    const auto r = FA_RSRC(Kh + (size_t)kv0 * rsk, bytes);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       // (the LDS pointer goes through a local: written inline as the builtin's
       // argument, the host compilation pass drops the kernel launch stubs)
       lds_char* const lp = dst + dma_lds_k<C>(wave, i);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, kdo0 + i * C::dmaStrideK, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, kdo0 + i * dsk, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void dma_v(lds_char* dst, int t, int limit = 0x7fffffff) const {
     const int kv0 = t * BN;
-    const uint32_t bytes = t < limit ? (uint32_t)(S - kv0) * RB : 0u;
-    const auto r = FA_RSRC(Vh + (size_t)kv0 * D, bytes);
+    const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsv : 0u;
+    const auto r = FA_RSRC(Vh + (size_t)kv0 * rsv, bytes);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       lds_char* const lp = dst + dma_lds_v<C>(wave, i);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, vdo0 + i * C::dmaStrideV, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, vdo0 + i * dsv, 0, 0, 0);
     }
   }
 
@@ -302,7 +364,7 @@ struct Wave {
   }
   // the tile starting at key kv0 needs index compares (diagonal or ragged end)
   __device__ __forceinline__ bool needs_mask(int kv0) const {
-    return (CAUSAL && kv0 + BN - 1 > q0w) || kv0 + BN > S;
+    return (CAUSAL && kv0 + BN - 1 > q0w + off) || kv0 + BN > Lk;
   }
   __device__ __forceinline__ void mask(f32x16 (&s)[NKB], int kv0) const {
 #pragma unroll
@@ -310,7 +372,7 @@ struct Wave {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + 32 * kb + acc_key32(r, hh);
-        const bool vis = key < S && (!CAUSAL || key <= qrow);
+        const bool vis = key < Lk && (!CAUSAL || key <= qrow + off);
         s[kb][r] = vis ? s[kb][r] : -INFINITY;
       }
   }
@@ -350,7 +412,7 @@ struct Wave {
   }
   // rare path: some row of the wave moved its base -> rescale O
   __device__ __forceinline__ void rescale(int j, float hist) {
-    if (DIAG && j >= 1 && hh == 0 && qrow < S && hist < 1.f) ++n_events;
+    if (DIAG && j >= 1 && hh == 0 && qrow < Lq && hist < 1.f) ++n_events;
     if (j >= 1 && __builtin_amdgcn_ballot_w64(hist < 1.f) != 0) {
 #pragma unroll
       for (int jd = 0; jd < NDB; ++jd) o[jd] *= hist;
@@ -365,14 +427,15 @@ struct Wave {
     softmax_exp(s, p);
   }
 
-  // normalise once, write O and lse (rows past S dropped by the range check)
-  __device__ __forceinline__ void epilogue(T* O, float* LSE, unsigned long long* events) {
+  // normalise once, write O and lse (rows past Lq dropped by the range
+  // check). A row that sees no key (possible when Lk < Lq under the causal
+  // mask, or Lk = 0) gets O = 0 and lse = -inf.
+  __device__ __forceinline__ void epilogue(unsigned long long* events) {
     const float ltot = sum_xor32(lsum);
-    if (q0w < S) {
-      const size_t head = (size_t)bh * (size_t)S * D;
-      const auto ro = FA_RSRC(O + head, (uint32_t)S * RB);
-      const auto rl = FA_RSRC(LSE + (size_t)bh * S, (uint32_t)S * 4u);
-      const float inv = 1.f / ltot;
+    if (q0w < Lq) {
+      const auto ro = FA_RSRC(Oh, (uint32_t)Lq * rso);
+      const auto rl = FA_RSRC(Lh, (uint32_t)Lq * 4u);
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
 #pragma unroll
       for (int jd = 0; jd < NDB; ++jd)
 #pragma unroll
@@ -384,10 +447,10 @@ struct Wave {
                            Ops<T>::pack2(a[r0 + 4] * inv, a[r0 + 5] * inv),
                            Ops<T>::pack2(a[r0 + 6] * inv, a[r0 + 7] * inv)};
           // accumulator element r0+e of lane (i, hh) is d = 32jd + 16g + 8hh + e
-          __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_frag_off<D>(qrow, jd, g, hh), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_frag_off<D>(qrow, jd, g, hh, rso), 0, 0);
         }
       if (hh == 0) {
-        const float l2 = (b + __builtin_amdgcn_logf(ltot)) * kLn2;
+        const float l2 = ltot > 0.f ? (b + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l2), rl,
                                               (uint32_t)qrow * 4u, 0, 0);
       }
@@ -406,9 +469,7 @@ template <int R, class X> __device__ __forceinline__ X pick3(X a, X b, X c) {
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-          T* __restrict__ O, float* __restrict__ LSE, int BH, int S, int nqt, float c,
-          unsigned long long* __restrict__ events) {
+fa_fwd_pp(const Problem P) {
   using C = Cfg8<D>;
   using W = Wave<T, C, CAUSAL, THR, DIAG>;
   constexpr int TB = C::tileBytes;
@@ -436,7 +497,7 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   lds_char* const lv2 = (lds_char*)a_vstage2;
 
   W w;
-  w.init(Q, K, V, BH, S, nqt, c);
+  if (!w.init(P)) return;
   const int grp = w.wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   const int ntiles = w.group_tiles();
   const int nw = w.wave_tiles();
@@ -529,7 +590,7 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   if (grp == 0) run(IC<0>{});
   else run(IC<1>{});
   __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the work-group
-  w.epilogue(O, LSE, events);
+  w.epilogue(P.events);
 }
 
 // ------------------------------------------------- four waves x 64 rows
@@ -547,9 +608,7 @@ fa_fwd_pp(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
-fa_fwd_w2(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-          T* __restrict__ O, float* __restrict__ LSE, int BH, int S, int nqt, float c,
-          unsigned long long* __restrict__ events) {
+fa_fwd_w2(const Problem P) {
   using C = CfgW2<D>;
   using W = Wave<T, C, CAUSAL, THR, DIAG>;
   constexpr int TB = C::tileBytes;
@@ -572,8 +631,8 @@ fa_fwd_w2(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   lds_char* const lv2 = (lds_char*)a_vstage2;
 
   W wa, wb;
-  wa.init(Q, K, V, BH, S, nqt, c, 0);
-  wb.init(Q, K, V, BH, S, nqt, c, 1);
+  if (!wa.init(P, 0)) return;
+  wb.init(P, 1);
   const int ntiles = wa.group_tiles();
   // tiles either block computes (block B's rows can lie wholly past S)
   const int nlast = max(wa.wave_tiles(), wb.wave_tiles());
@@ -692,8 +751,8 @@ fa_fwd_w2(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
     if (j + 6 > ntiles) break;
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the work-group
-  wa.epilogue(O, LSE, events);
-  wb.epilogue(O, LSE, events);
+  wa.epilogue(P.events);
+  wb.epilogue(P.events);
 }
 
 // ------------------------------------------------------------ four-wave
@@ -707,9 +766,7 @@ template <int D> struct Pipe { static constexpr bool three = D == 64; };
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa_fwd_k4(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-          T* __restrict__ O, float* __restrict__ LSE, int BH, int S, int nqt, float c,
-          unsigned long long* __restrict__ events) {
+fa_fwd_k4(const Problem P) {
   using C = Cfg4<D>;
   using W = Wave<T, C, CAUSAL, THR, DIAG>;
   constexpr bool P3 = Pipe<D>::three;
@@ -726,7 +783,7 @@ fa_fwd_k4(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   lds_char* const lv1 = (lds_char*)a_vstage1;
 
   W w;
-  w.init(Q, K, V, BH, S, nqt, c);
+  if (!w.init(P)) return;
   const int ntiles = w.group_tiles();
   const int nw = w.wave_tiles();
 
@@ -818,7 +875,7 @@ fa_fwd_k4(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict_
   }
   if (j < niter) iter(IC<0>{}, j);
 
-  w.epilogue(O, LSE, events);
+  w.epilogue(P.events);
 }
 
 // ------------------------------------------------------------------- host
@@ -836,80 +893,152 @@ template <int D> static bool use_pingpong(int BH, int S, int variant) {
 }
 
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
-static int launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int S, float scale, hipStream_t stream, unsigned long long* ev,
-                      int variant) {
-  const int BH = B * H;
-  const float c = scale * kLog2e;
+static int launch_one(Problem P, hipStream_t stream, int variant) {
+  const int BH = P.B * P.H;
   if (variant == kTwoBlock) {
-    const int nqt = num_q_tiles(S, CfgW2<D>::BM);
-    hipLaunchKernelGGL((fa_fwd_w2<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)nqt * (unsigned)BH),
-                       dim3(CfgW2<D>::threads), 0, stream, (const T*)q, (const T*)k, (const T*)v,
-                       (T*)o, lse, BH, S, nqt, c, ev);
-  } else if (use_pingpong<D>(BH, S, variant)) {
-    const int nqt = num_q_tiles(S, Cfg8<D>::BM);
-    hipLaunchKernelGGL((fa_fwd_pp<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)nqt * (unsigned)BH),
-                       dim3(Cfg8<D>::threads), 0, stream, (const T*)q, (const T*)k, (const T*)v,
-                       (T*)o, lse, BH, S, nqt, c, ev);
+    P.nqt = num_q_tiles(P.Sq, CfgW2<D>::BM);
+    hipLaunchKernelGGL((fa_fwd_w2<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+                       dim3(CfgW2<D>::threads), 0, stream, P);
+  } else if (use_pingpong<D>(BH, P.Sq, variant)) {
+    P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);
+    hipLaunchKernelGGL((fa_fwd_pp<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+                       dim3(Cfg8<D>::threads), 0, stream, P);
   } else {
-    const int nqt = num_q_tiles(S, Cfg4<D>::BM);
-    hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)nqt * (unsigned)BH),
-                       dim3(Cfg4<D>::threads), 0, stream, (const T*)q, (const T*)k, (const T*)v,
-                       (T*)o, lse, BH, S, nqt, c, ev);
+    P.nqt = num_q_tiles(P.Sq, Cfg4<D>::BM);
+    hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+                       dim3(Cfg4<D>::threads), 0, stream, P);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-template <typename T, int D, int THR, bool DIAG>
-static int launch_c(int causal, const void* q, const void* k, const void* v, void* o, float* lse,
-                    int B, int H, int S, float scale, hipStream_t st, unsigned long long* ev,
-                    int variant) {
-  return causal
-             ? launch_one<T, D, true, THR, DIAG>(q, k, v, o, lse, B, H, S, scale, st, ev, variant)
-             : launch_one<T, D, false, THR, DIAG>(q, k, v, o, lse, B, H, S, scale, st, ev, variant);
-}
-
 template <typename T, int THR, bool DIAG>
-static int launch_d(int D, int causal, const void* q, const void* k, const void* v, void* o,
-                    float* lse, int B, int H, int S, float scale, hipStream_t st,
-                    unsigned long long* ev, int variant) {
-  return D == 64 ? launch_c<T, 64, THR, DIAG>(causal, q, k, v, o, lse, B, H, S, scale, st, ev,
-                                              variant)
-                 : launch_c<T, 128, THR, DIAG>(causal, q, k, v, o, lse, B, H, S, scale, st, ev,
-                                               variant);
+static int launch(const Problem& P, int D, int causal, hipStream_t st, int variant) {
+  if (D == 64)
+    return causal ? launch_one<T, 64, true, THR, DIAG>(P, st, variant)
+                  : launch_one<T, 64, false, THR, DIAG>(P, st, variant);
+  return causal ? launch_one<T, 128, true, THR, DIAG>(P, st, variant)
+                : launch_one<T, 128, false, THR, DIAG>(P, st, variant);
 }
 
-static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
+static int launch_dtype(const Problem& P, int D, int causal, int dtype, hipStream_t st) {
+  return dtype == FA_BF16 ? launch<__bf16, 8, false>(P, D, causal, st, kAuto)
+                          : launch<_Float16, 8, false>(P, D, causal, st, kAuto);
 }
 
-// Host-side validation; touches no HIP API.
-static int validate(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                    int H, int S, int D, int causal, float scale, int dtype, bool* empty) {
-  *empty = false;
+// ------------------------------------------------------- host validation
+// Touches no HIP API.
+
+// Byte span [lo, hi) of a strided tensor: dims n[i] with strides st[i]
+// (elements), the innermost extent `inner` elements, element size es.
+struct Span {
+  uintptr_t lo, hi;
+};
+static Span span_of(const void* base, const long long* n, const long long* st, int nd,
+                    long long inner, int es) {
+  long long last = inner;  // one past the last element, relative to base
+  for (int i = 0; i < nd; ++i) last += (n[i] - 1) * st[i];
+  return {(uintptr_t)base, (uintptr_t)base + (uintptr_t)(last * es)};
+}
+static bool spans_overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// True when no two index tuples of dims n (strides st, all >= 0) with an
+// innermost block of `inner` contiguous elements share an element: sorted by
+// stride, each stride must clear the whole extent of the smaller ones.
+static bool no_self_overlap(const long long* n, const long long* st, int nd, long long inner) {
+  long long dn[4], ds[4];
+  int m = 0;
+  for (int i = 0; i < nd; ++i)
+    if (n[i] > 1) {
+      dn[m] = n[i];
+      ds[m] = st[i];
+      ++m;
+    }
+  for (int i = 1; i < m; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && ds[j] < ds[j - 1]; --j) {
+      const long long t = ds[j]; ds[j] = ds[j - 1]; ds[j - 1] = t;
+      const long long u = dn[j]; dn[j] = dn[j - 1]; dn[j - 1] = u;
+    }
+  long long extent = inner;
+  for (int i = 0; i < m; ++i) {
+    if (ds[i] < extent) return false;
+    extent = ds[i] * (dn[i] - 1) + extent;
+  }
+  return true;
+}
+
+// Scalar checks shared by every entry point.
+static int validate_args(int B, int H, int Sq, int Sk, int D, int causal, float scale, int dtype) {
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (B < 0 || H < 0 || S < 0) return FA_ERR_DIM;
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return FA_ERR_DIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
-  if ((long long)B * H * S == 0) {
+  if ((long long)B * H * num_q_tiles(Sq, Cfg4<64>::BM) >= (1LL << 31)) return FA_ERR_DIM;
+  return FA_OK;
+}
+
+// Checks on a filled Problem (non-empty). rows_q / rows_k: the query and key
+// row counts of each tensor's outer dims, as (n, stride) pairs per dim.
+static int validate_problem(const Problem& P, int D, const long long* nq, const long long* sq_,
+                            const long long* sk_, const long long* sv_, const long long* so_,
+                            const long long* nk, int nd, const long long* nl,
+                            const long long* sl, int ndl) {
+  if (!P.q || !P.k || !P.v || !P.o || !P.lse) return FA_ERR_NULL;
+  const uintptr_t al = (uintptr_t)P.q | (uintptr_t)P.k | (uintptr_t)P.v | (uintptr_t)P.o |
+                       (uintptr_t)P.lse;
+  if (al & 15) return FA_ERR_ALIGN;
+  const long long all[] = {P.qb, P.qh, P.qs, P.kb, P.kh, P.ks, P.vb,
+                           P.vh, P.vs, P.ob, P.oh, P.os, P.lb, P.lh};
+  for (long long x : all)
+    if (x < 0) return FA_ERR_LAYOUT;
+  for (int i = 0; i < 12; ++i)
+    if (all[i] % 8) return FA_ERR_ALIGN;  // every row starts 16-byte aligned
+  if (P.qs < D || P.ks < D || P.vs < D || P.os < D) return FA_ERR_LAYOUT;
+  // offsets within one (sequence, head) are 32-bit bytes
+  const long long lim = 1LL << 31;
+  if ((long long)P.Sq * P.qs * 2 >= lim || (long long)P.Sk * P.ks * 2 >= lim ||
+      (long long)P.Sk * P.vs * 2 >= lim || (long long)P.Sq * P.os * 2 >= lim ||
+      (long long)P.Sq * 4 >= lim)
+    return FA_ERR_DIM;
+  if (!no_self_overlap(nq, so_, nd, D) || !no_self_overlap(nl, sl, ndl, 1)) return FA_ERR_LAYOUT;
+  const Span q = span_of(P.q, nq, sq_, nd, D, 2), k = span_of(P.k, nk, sk_, nd, D, 2),
+             v = span_of(P.v, nk, sv_, nd, D, 2), o = span_of(P.o, nq, so_, nd, D, 2),
+             l = span_of(P.lse, nl, sl, ndl, 1, 4);
+  if (spans_overlap(o, q) || spans_overlap(o, k) || spans_overlap(o, v) || spans_overlap(l, q) ||
+      spans_overlap(l, k) || spans_overlap(l, v) || spans_overlap(l, o))
+    return FA_ERR_ALIAS;
+  if ((uint64_t)(o.hi - o.lo) >> 41 || (uint64_t)(q.hi - q.lo) >> 41) return FA_ERR_DIM;  // 2^40 elements
+  return FA_OK;
+}
+
+// Fixed-length problem from strides (14: q, k, v, o as batch, head, row; lse
+// as batch, head). *empty is set when there is no query row to compute.
+static int make_fixed(Problem* P, const void* q, const void* k, const void* v, void* o,
+                      float* lse, int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                      int dtype, const long long* st, bool* empty) {
+  *empty = false;
+  int r = validate_args(B, H, Sq, Sk, D, causal, scale, dtype);
+  if (r != FA_OK) return r;
+  if ((long long)B * H * Sq == 0) {
     *empty = true;
     return FA_OK;
   }
-  if ((long long)S * D * 2 >= (1LL << 31)) return FA_ERR_DIM;  // 32-bit buffer offsets
-  const long long rows = (long long)B * H * S;
-  if (rows * D > (1LL << 40)) return FA_ERR_DIM;
-  if ((long long)B * H * num_q_tiles(S, Cfg4<64>::BM) >= (1LL << 31)) return FA_ERR_DIM;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
-  if (al & 15) return FA_ERR_ALIGN;
-  const size_t nt = (size_t)rows * D * 2, nl = (size_t)rows * 4;
-  if (overlaps(o, nt, q, nt) || overlaps(o, nt, k, nt) || overlaps(o, nt, v, nt) ||
-      overlaps(lse, nl, q, nt) || overlaps(lse, nl, k, nt) || overlaps(lse, nl, v, nt) ||
-      overlaps(lse, nl, o, nt))
-    return FA_ERR_ALIAS;
-  return FA_OK;
+  if (!st) return FA_ERR_NULL;
+  *P = Problem{q, k, v, o, lse, st[0], st[1], st[2], st[3], st[4], st[5], st[6],
+               st[7], st[8], st[9], st[10], st[11], st[12], st[13], nullptr, nullptr,
+               0, 0, B, H, Sq, Sk, 0, scale * kLog2e, nullptr};
+  const long long nq[] = {B, H, Sq}, nk[] = {B, H, Sk > 0 ? Sk : 1};
+  const long long sq_[] = {st[0], st[1], st[2]}, sk_[] = {st[3], st[4], st[5]},
+                  sv_[] = {st[6], st[7], st[8]}, so_[] = {st[9], st[10], st[11]};
+  const long long nl[] = {B, H, Sq}, sl[] = {st[12], st[13], 1};
+  return validate_problem(*P, D, nq, sq_, sk_, sv_, so_, nk, 3, nl, sl, 3);
+}
+
+static void dense_strides(long long* st, int H, int S, int D) {
+  const long long hs = (long long)S * D;
+  const long long v[] = {H * hs, hs, D, H * hs, hs, D, H * hs, hs, D, H * hs, hs, D,
+                         (long long)H * S, S};
+  for (int i = 0; i < 14; ++i) st[i] = v[i];
 }
 
 }  // namespace fa
@@ -918,14 +1047,13 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S,
            int D, int causal, float scale, hipStream_t stream, int dtype) {
+  long long st[14];
+  fa::dense_strides(st, H, S, D);
+  fa::Problem P;
   bool empty;
-  const int st = fa::validate(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, &empty);
-  if (st != FA_OK || empty) return st;
-  return dtype == FA_BF16
-             ? fa::launch_d<__bf16, 8, false>(D, causal, q, k, v, o, lse, B, H, S, scale, stream,
-                                              nullptr, fa::kAuto)
-             : fa::launch_d<_Float16, 8, false>(D, causal, q, k, v, o, lse, B, H, S, scale,
-                                                stream, nullptr, fa::kAuto);
+  const int r = fa::make_fixed(&P, q, k, v, o, lse, B, H, S, S, D, causal, scale, dtype, st, &empty);
+  if (r != FA_OK || empty) return r;
+  return fa::launch_dtype(P, D, causal, dtype, stream);
 }
 
 int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -938,27 +1066,62 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse
   return fa_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, stream, FA_BF16);
 }
 
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int Sq, int Sk, int D, int causal, float scale, hipStream_t stream,
+                   int dtype, const long long* strides) {
+  fa::Problem P;
+  bool empty;
+  const int r =
+      fa::make_fixed(&P, q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype, strides, &empty);
+  if (r != FA_OK || empty) return r;
+  return fa::launch_dtype(P, D, causal, dtype, stream);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                  int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int D,
+                  int causal, float scale, hipStream_t stream, int dtype,
+                  const long long* strides) {
+  int r = fa::validate_args(B, H, max_seqlen_q, max_seqlen_k, D, causal, scale, dtype);
+  if (r != FA_OK) return r;
+  if (total_q < 0 || total_k < 0) return FA_ERR_DIM;
+  if ((long long)B * H * max_seqlen_q == 0 || total_q == 0) return FA_OK;
+  if (!cu_seqlens_q || !cu_seqlens_k || !strides) return FA_ERR_NULL;
+  if (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3) return FA_ERR_ALIGN;
+  const long long* st = strides;  // q, k, v, o as head, row; lse as head
+  fa::Problem P{q, k, v, o, lse, 0, st[0], st[1], 0, st[2], st[3], 0, st[4], st[5], 0,
+                st[6], st[7], 0, st[8], cu_seqlens_q, cu_seqlens_k, total_q, total_k,
+                B, H, max_seqlen_q, max_seqlen_k, 0, scale * fa::kLog2e, nullptr};
+  const long long nq[] = {H, total_q}, nk[] = {H, total_k > 0 ? total_k : 1};
+  const long long sq_[] = {st[0], st[1]}, sk_[] = {st[2], st[3]}, sv_[] = {st[4], st[5]},
+                  so_[] = {st[6], st[7]};
+  const long long nl[] = {H, total_q}, sl[] = {st[8], 1};
+  r = fa::validate_problem(P, D, nq, sq_, sk_, sv_, so_, nk, 2, nl, sl, 2);
+  if (r != FA_OK) return r;
+  return fa::launch_dtype(P, D, causal, dtype, stream);
+}
+
 int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int S, int D, int causal, float scale, hipStream_t stream, int dtype,
                 int threshold_log2, int variant, unsigned long long* rescale_events) {
+  long long st[14];
+  fa::dense_strides(st, H, S, D);
+  fa::Problem P;
   bool empty;
-  const int st = fa::validate(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, &empty);
-  if (st != FA_OK) return st;
+  const int r = fa::make_fixed(&P, q, k, v, o, lse, B, H, S, S, D, causal, scale, dtype, st, &empty);
+  if (r != FA_OK) return r;
   if (threshold_log2 != 0 && threshold_log2 != 8) return FA_ERR_ARG;
   if (variant < fa::kAuto || variant > fa::kTwoBlock) return FA_ERR_ARG;
   if (!rescale_events) return FA_ERR_NULL;
   if (((uintptr_t)rescale_events & 7) != 0) return FA_ERR_ALIGN;
   if (empty) return FA_OK;
+  P.events = rescale_events;
   const bool bf = dtype == FA_BF16;
   if (threshold_log2 == 8)
-    return bf ? fa::launch_d<__bf16, 8, true>(D, causal, q, k, v, o, lse, B, H, S, scale, stream,
-                                              rescale_events, variant)
-              : fa::launch_d<_Float16, 8, true>(D, causal, q, k, v, o, lse, B, H, S, scale,
-                                                stream, rescale_events, variant);
-  return bf ? fa::launch_d<__bf16, 0, true>(D, causal, q, k, v, o, lse, B, H, S, scale, stream,
-                                            rescale_events, variant)
-            : fa::launch_d<_Float16, 0, true>(D, causal, q, k, v, o, lse, B, H, S, scale, stream,
-                                              rescale_events, variant);
+    return bf ? fa::launch<__bf16, 8, true>(P, D, causal, stream, variant)
+              : fa::launch<_Float16, 8, true>(P, D, causal, stream, variant);
+  return bf ? fa::launch<__bf16, 0, true>(P, D, causal, stream, variant)
+            : fa::launch<_Float16, 0, true>(P, D, causal, stream, variant);
 }
 
 int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n, int* threads,
@@ -987,10 +1150,11 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIAS: return "o or lse overlaps another buffer";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case FA_ERR_ARG: return "causal must be 0 or 1 (or a diagnostic argument is invalid)";
+    case FA_ERR_LAYOUT: return "a stride is negative, a row stride is below D, or output rows overlap";
     default: return "unknown status";
   }
 }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"

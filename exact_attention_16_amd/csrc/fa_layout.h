@@ -41,8 +41,9 @@ template <int D_, int NW_, int BN_, int RPW_ = kRowsPerWave> struct Cfg {
   static constexpr int chunks = D / 8;                   // 16-byte chunks per row
   static constexpr int tileBytes = BN * rowBytes;        // one K or V tile
   static constexpr int dmaPerWave = tileBytes / 1024 / NW;  // 1-KiB DMA issues per wave
-  static constexpr uint32_t dmaStrideK = NW * 1024u;     // source step per K issue
-  static constexpr uint32_t dmaStrideV = 1024u;          // source step per V issue
+  static constexpr int rowsPerBlock = 64 / chunks;       // rows filled by one DMA issue
+  static constexpr int dmaRowsK = NW * rowsPerBlock;     // source rows between K issues
+  static constexpr int dmaRowsV = rowsPerBlock;          // source rows between V issues
   static_assert(tileBytes % (1024 * NW) == 0, "tile must split into whole DMA issues");
   static_assert(BN % 32 == 0, "KV tile must be whole 32-key MFMA blocks");
   static_assert(RPW % kRowsPerWave == 0, "a wave owns whole 32-row blocks");
@@ -85,16 +86,28 @@ FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh
 
 FA_HD int num_q_tiles(int S, int BM) { return (S + BM - 1) / BM; }
 
+// Causal masks are aligned bottom-right: with Lq queries and Lk keys, query i
+// sees keys j <= i + (Lk - Lq). With Lq == Lk that is j <= i.
+FA_HD int clamp_keys(int e, int Lk) { return e < 0 ? 0 : (e < Lk ? e : Lk); }
+
 // Exclusive upper bound of the keys a work-group's Q tile can see.
-FA_HD int tile_kv_end(int qt, int S, bool causal, int BM) {
-  const int e = causal ? (qt + 1) * BM : S;
-  return e < S ? e : S;
+FA_HD int tile_kv_end(int qt, int Lq, int Lk, bool causal, int BM) {
+  return causal ? clamp_keys((qt + 1) * BM + (Lk - Lq), Lk) : Lk;
 }
 
 // Exclusive upper bound of the keys visible to any row of one wave.
-FA_HD int wave_kv_end(int q0w, int S, bool causal) {
-  const int e = causal ? q0w + kRowsPerWave : S;
-  return e < S ? e : S;
+FA_HD int wave_kv_end(int q0w, int Lq, int Lk, bool causal) {
+  return causal ? clamp_keys(q0w + kRowsPerWave + (Lk - Lq), Lk) : Lk;
+}
+
+// Leading KV tiles of BN keys that need no index compares for a wave whose
+// first row is q0w: tiles whose last key that row sees (causal) and that end
+// before the last key.
+FA_HD int unmasked_tiles(int q0w, int Lq, int Lk, bool causal, int BN) {
+  const int r = Lk / BN;
+  const int e = q0w + (Lk - Lq) + 1;  // keys visible to row q0w
+  const int d = e < 0 ? 0 : e / BN;
+  return causal ? (d < r ? d : r) : r;
 }
 
 // --------------------------------------------------------- LDS swizzles
@@ -131,11 +144,13 @@ template <int D> FA_HD uint32_t v_off(int r, int c) {
 // so each DMA issue fills one 1-KiB block of the tile. Lane p fetches the
 // logical chunk that belongs at its LDS slot; dma_src_* return that chunk's
 // byte offset within the (contiguous) global tile.
+// Source rows are rs bytes apart (rowBytes for dense rows, more for strided
+// layouts).
 // K: issue i of wave w fills block i*NW + w, so successive issues are NW
 // blocks (a multiple of 16 rows) apart and gk, which reads row bits 0..3,
-// repeats: the source offset of issue i is issue 0's plus i*NW*1024 bytes.
+// repeats: the source offset of issue i is issue 0's plus i*dmaRowsK*rs.
 // V: issue i of wave w fills block w*dmaPerWave + i; gv reads row bits 0..1
-// only, so issue i is issue 0's plus i*1024 bytes.
+// only, so issue i is issue 0's plus i*dmaRowsV*rs.
 template <class C> FA_HD int dma_block_k(int w, int i) { return i * C::NW + w; }
 template <class C> FA_HD int dma_block_v(int w, int i) { return w * C::dmaPerWave + i; }
 template <class C> FA_HD void dma_slot(int block, int lane, int* r, int* pc) {
@@ -143,15 +158,15 @@ template <class C> FA_HD void dma_slot(int block, int lane, int* r, int* pc) {
   *r = idx / C::chunks;
   *pc = idx % C::chunks;
 }
-template <class C> FA_HD uint32_t dma_src_k(int w, int i, int lane) {
+template <class C> FA_HD uint32_t dma_src_k(int w, int i, int lane, uint32_t rs = C::rowBytes) {
   int r, pc;
   dma_slot<C>(dma_block_k<C>(w, i), lane, &r, &pc);
-  return (uint32_t)(r * C::rowBytes + ((pc ^ gk<C::D>(r)) << 4));
+  return (uint32_t)r * rs + (uint32_t)((pc ^ gk<C::D>(r)) << 4);
 }
-template <class C> FA_HD uint32_t dma_src_v(int w, int i, int lane) {
+template <class C> FA_HD uint32_t dma_src_v(int w, int i, int lane, uint32_t rs = C::rowBytes) {
   int r, pc;
   dma_slot<C>(dma_block_v<C>(w, i), lane, &r, &pc);
-  return (uint32_t)(r * C::rowBytes + ((pc ^ gv<C::D>(r)) << 4));
+  return (uint32_t)r * rs + (uint32_t)((pc ^ gv<C::D>(r)) << 4);
 }
 template <class C> FA_HD uint32_t dma_lds_k(int w, int i) { return (uint32_t)dma_block_k<C>(w, i) * 1024u; }
 template <class C> FA_HD uint32_t dma_lds_v(int w, int i) { return (uint32_t)dma_block_v<C>(w, i) * 1024u; }
@@ -203,13 +218,13 @@ template <int D> FA_HD uint32_t v_tr_off(int jd, int kc, int rd, int lane) {
 
 // ------------------------------------------ global byte offsets (per head)
 // Q operand fragment j of a lane: row qrow, d = 16*j + 8*hh + 0..7.
-template <int D> FA_HD uint32_t q_frag_off(int qrow, int j, int hh) {
-  return (uint32_t)(qrow * D * 2 + (16 * j + 8 * hh) * 2);
+template <int D> FA_HD uint32_t q_frag_off(int qrow, int j, int hh, uint32_t rs = D * 2) {
+  return (uint32_t)qrow * rs + (uint32_t)((16 * j + 8 * hh) * 2);
 }
 // O store of a lane: row qrow, d = 32*jd + 16*g + 8*hh + 0..7 (accumulator
 // elements 8*g .. 8*g+7 of d-block jd).
-template <int D> FA_HD uint32_t o_frag_off(int qrow, int jd, int g, int hh) {
-  return (uint32_t)(qrow * D * 2 + (32 * jd + 16 * g + 8 * hh) * 2);
+template <int D> FA_HD uint32_t o_frag_off(int qrow, int jd, int g, int hh, uint32_t rs = D * 2) {
+  return (uint32_t)qrow * rs + (uint32_t)((32 * jd + 16 * g + 8 * hh) * 2);
 }
 
 // ------------------------------------- ping-pong schedule (eight waves)

@@ -59,7 +59,9 @@ typedef enum {
   FA_ERR_SCALE = -5,       /* scale not finite or not > 0                   */
   FA_ERR_ALIAS = -6,       /* o or lse overlaps another buffer              */
   FA_ERR_HIP = -7,         /* the HIP runtime rejected the launch           */
-  FA_ERR_ARG = -8          /* causal not 0/1, or a bad diagnostic argument  */
+  FA_ERR_ARG = -8,         /* causal not 0/1, or a bad diagnostic argument  */
+  FA_ERR_LAYOUT = -9       /* a stride is negative, a row stride < D, or an
+                              output's rows overlap each other             */
 } fa_status_t;
 
 /*
@@ -96,6 +98,69 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse
                 hipStream_t stream);
 
 /*
+ * fa_fwd_strided -- fa_fwd over strided tensors, with separate query and key
+ * lengths. The kernel signature of "CUDA手写masked multi-head attention性能
+ * 优化实战" (section 4.2) takes per-tensor strides; this entry point accepts
+ * any layout whose rows are D contiguous elements.
+ *
+ *   q, o     device, element (b, h, i, d) at base + b*sb + h*sh + i*ss + d,
+ *            i < Sq
+ *   k, v     device, element (b, h, j, d) likewise, j < Sk
+ *   lse      device float, element (b, h, i) at lse + b*lb + h*lh + i
+ *   strides  host array of 14 element strides, read during the call:
+ *            q (sb, sh, ss), k (sb, sh, ss), v (sb, sh, ss), o (sb, sh, ss),
+ *            lse (lb, lh). All >= 0. The 12 tensor strides are multiples
+ *            of 8 (every row 16-byte aligned) and each row stride is >= D.
+ *   Sq, Sk   >= 0. B*H*Sq == 0 is a no-op returning FA_OK.
+ *   causal   1: key j visible to query i iff j <= i + (Sk - Sq), the mask
+ *            aligned to the last query and the last key (with Sq == Sk,
+ *            j <= i). A query that sees no key gets O = 0 and lse = -inf.
+ *   other arguments as for fa_fwd.
+ *
+ * Limits: Sq*ss*2 and Sk*ss*2 < 2^31 for each tensor's row stride ss (one
+ * (sequence, head) addressed with 32-bit offsets). Errors: negative or
+ * overlapping-output strides FA_ERR_LAYOUT; strides not multiples of 8
+ * FA_ERR_ALIGN; o or lse sharing bytes with q, k, v or each other (by the
+ * byte ranges the strides span) FA_ERR_ALIAS; the rest as for fa_fwd.
+ * k and v may alias each other or q (all read only); a zero head stride on
+ * k and v shares one key/value head across all query heads.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                   hipStream_t stream, int dtype, const long long* strides);
+
+/*
+ * fa_fwd_varlen -- attention forward over B sequences of different lengths
+ * packed along one token axis: dynamic sequence lengths without padding
+ * (the shape-dependent dispatch of "CUDA手写masked multi-head attention性能
+ * 优化实战", section 6.3, done here with per-sequence offsets in one launch).
+ *
+ *   cu_seqlens_q, cu_seqlens_k   device int arrays of B+1 token offsets,
+ *            non-decreasing: sequence b has query tokens cu_seqlens_q[b] ..
+ *            cu_seqlens_q[b+1]-1 and key tokens cu_seqlens_k[b] ..
+ *            cu_seqlens_k[b+1]-1. Read by the kernel; owned by the caller.
+ *   max_seqlen_q, max_seqlen_k   upper bounds of the lengths (they size the
+ *            grid; a longer sequence is cut to them).
+ *   total_q, total_k   token rows q/o/lse and k/v hold; the kernel clamps
+ *            every offset to them, so a bad offset array cannot address
+ *            memory outside the tensors.
+ *   q, o     element (token t, head h, d) at base + t*ss + h*sh + d
+ *   k, v     likewise, t < total_k
+ *   lse      float, element (h, t) at lse + h*lh + t
+ *   strides  host array of 9 element strides: q (sh, ss), k (sh, ss),
+ *            v (sh, ss), o (sh, ss), lse (lh); for the common packed layout
+ *            [total, H, D]: sh = D, ss = H*D, and lh = total_q.
+ *   causal   as for fa_fwd_strided, per sequence (j <= i + Lk - Lq).
+ *   other arguments, limits (with the maxima as Sq, Sk) and errors as for
+ *   fa_fwd_strided; misaligned cu_seqlens pointers FA_ERR_ALIGN.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H,
+                  int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                  int D, int causal, float scale, hipStream_t stream, int dtype,
+                  const long long* strides);
+
+/*
  * fa_fwd_diag -- diagnostic variant of fa_fwd for tests.
  *
  * Same arguments and result as fa_fwd, plus:
@@ -127,8 +192,10 @@ int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse
  * fa_fwd_tile -- the tile shape fa_fwd uses for a call with (B, H, S) at
  * head dimension D: query rows per work-group, keys per KV tile, threads per
  * work-group, and the number of work-groups launched. fa_fwd runs the
- * eight-wave kernel (256 rows; 64 keys per tile at D=128, 128 at D=64) when
+ * eight-wave kernel (256 rows; 96 keys per tile at D=128, 128 at D=64) when
  * B*H*ceil(S/256) >= 256, else the four-wave kernel (128 rows, 64 keys).
+ * The same choice, with S the query length, applies to fa_fwd_strided and
+ * fa_fwd_varlen.
  * Any output pointer may be NULL. Returns FA_ERR_UNSUPPORTED for D not in
  * {64, 128}.
  */

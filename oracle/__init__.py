@@ -10,16 +10,17 @@ arithmetic).
 Contents:
 
 * :mod:`oracle.attention` -- the plain definition of exact attention in
-  float64, materialising the full score matrix, plus a pure-Python brute force
-  for tiny inputs.
+  float64, materialising the full score matrix (also for query and key
+  lengths that differ and for sequences packed along a token axis), plus a
+  pure-Python brute force for tiny inputs.
 * :mod:`oracle.online` -- the streaming (tiled, online-softmax) algorithm with
   the lagging-max conditional rescale, in float64, step by step in the pages'
   order. It is used to check that the lagging-max algebra reaches the plain
   definition and to predict how often the rescale fires.
 """
 from .attention import (attention_fwd, attention_rows, attention_probs,
-                        attention_bruteforce)
+                        attention_bruteforce, attention_varlen)
 from .online import online_softmax_attention
 
 __all__ = ["attention_fwd", "attention_rows", "attention_probs",
-           "attention_bruteforce", "online_softmax_attention"]
+           "attention_bruteforce", "attention_varlen", "online_softmax_attention"]

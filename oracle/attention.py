@@ -3,10 +3,14 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may use this module; the product path never imports it.
 
-What is computed (per batch b and head h; Q, K, V are S x D):
+What is computed (per batch b and head h; Q is Sq x D, K and V are Sk x D):
 
-    X     = scale * Q K^T                     (S x S logits, materialised)
-    X_ij  = -inf  where causal and j > i      (key j visible iff j <= i)
+    X     = scale * Q K^T                     (Sq x Sk logits, materialised)
+    X_ij  = -inf  where causal and j > i + (Sk - Sq)
+                                              (key j visible iff j <= i + Sk - Sq:
+                                               the mask aligned to the last query
+                                               and the last key; with Sq == Sk,
+                                               j <= i)
     m_i   = max_j X_ij
     P_ij  = exp(X_ij - m_i),   l_i = sum_j P_ij
     O_i   = (sum_j P_ij V_j) / l_i
@@ -21,6 +25,12 @@ Sources:
   "FlashAttention的Triton性能考古学", section "核心算法回顾".
 * The row logsumexp output is not defined on the pages; it is taken here as
   the natural-log logsumexp of the scaled logits (a reading, not a quote).
+* The pages' causal mask is square. For Sq != Sk the mask is read as aligned
+  to the bottom-right corner (the last query sees every key), and a query
+  that sees no key (possible when Sk < Sq) is given O = 0 and lse = -inf
+  (readings; the pages are silent). Sequences of different lengths (the
+  dynamic-shape dispatch of the xdnf.cn page, section 6.3) are each the
+  definition applied to their own rows.
 
 Each step of the definition is its own small function so that a reader can
 check it against the formula above, and so that the pin tests can plant a
@@ -42,10 +52,10 @@ def _logits(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
     return scale * (q @ k.T)
 
 
-def _causal_mask(x: np.ndarray, rows: np.ndarray) -> np.ndarray:
-    """Key j is visible to query row i iff j <= i; hidden logits become -inf."""
+def _causal_mask(x: np.ndarray, rows: np.ndarray, offset: int = 0) -> np.ndarray:
+    """Key j is visible to query row i iff j <= i + offset; hidden logits become -inf."""
     j = np.arange(x.shape[1])
-    return np.where(j[None, :] > rows[:, None], -np.inf, x)
+    return np.where(j[None, :] > rows[:, None] + offset, -np.inf, x)
 
 
 def _row_max(x: np.ndarray) -> np.ndarray:
@@ -74,43 +84,87 @@ def _lse(m: np.ndarray, l: np.ndarray) -> np.ndarray:
 
 
 def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows,
-                   causal: bool, scale: float):
-    """O and LSE for selected query rows of one head (q, k, v: S x D float64).
+                   causal: bool, scale: float, offset: int | None = None):
+    """O and LSE for selected query rows of one head (q: Sq x D, k, v: Sk x D).
 
     Each row of attention depends only on its own query, so a subset of rows is
-    the definition restricted to those rows. Returns (O[R, D], lse[R]).
+    the definition restricted to those rows. ``offset`` is the causal
+    alignment (key j visible to row i iff j <= i + offset); by default
+    Sk - Sq. Rows that see no key get O = 0 and lse = -inf.
+    Returns (O[R, D], lse[R]).
     """
     rows = np.asarray(rows, dtype=np.int64)
+    if offset is None:
+        offset = k.shape[0] - q.shape[0]
+    D = q.shape[1]
+    if k.shape[0] == 0:
+        return np.zeros((len(rows), D)), np.full(len(rows), -np.inf)
     x = _logits(q[rows], k, scale)
     if causal:
-        x = _causal_mask(x, rows)
-    m = _row_max(x)
-    p = _exp_shifted(x, m)
-    l = _row_sum(p)
-    o = _normalise(p @ v, l)
-    return o, _lse(m, l)
+        x = _causal_mask(x, rows, offset)
+    seen = np.isfinite(x).any(axis=1)  # rows that see at least one key
+    o = np.zeros((len(rows), D))
+    lse = np.full(len(rows), -np.inf)
+    if seen.any():
+        xs = x[seen]
+        m = _row_max(xs)
+        p = _exp_shifted(xs, m)
+        l = _row_sum(p)
+        o[seen] = _normalise(p @ v, l)
+        lse[seen] = _lse(m, l)
+    return o, lse
 
 
 def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
                   scale: float):
-    """O and LSE for all rows; q, k, v of shape (..., S, D) in float64.
+    """O and LSE for all rows; q of shape (..., Sq, D), k and v (..., Sk, D), float64.
 
-    Returns O of shape (..., S, D) and lse of shape (..., S), float64.
-    One head at a time is materialised (an S x S float64 matrix).
+    Returns O of shape (..., Sq, D) and lse of shape (..., Sq), float64.
+    One head at a time is materialised (an Sq x Sk float64 matrix).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     lead = q.shape[:-2]
-    S, D = q.shape[-2:]
-    qf = q.reshape(-1, S, D)
-    kf = k.reshape(-1, S, D)
-    vf = v.reshape(-1, S, D)
+    Sq, D = q.shape[-2:]
+    Sk = k.shape[-2]
+    n = int(np.prod(lead, dtype=np.int64))
+    qf = q.reshape(n, Sq, D)
+    kf = k.reshape(n, Sk, D)
+    vf = v.reshape(n, Sk, D)
     o = np.empty_like(qf)
     lse = np.empty(qf.shape[:2], dtype=np.float64)
     for n in range(qf.shape[0]):
-        o[n], lse[n] = attention_rows(qf[n], kf[n], vf[n], np.arange(S), causal, scale)
-    return o.reshape(*lead, S, D), lse.reshape(*lead, S)
+        o[n], lse[n] = attention_rows(qf[n], kf[n], vf[n], np.arange(Sq), causal, scale)
+    return o.reshape(*lead, Sq, D), lse.reshape(*lead, Sq)
+
+
+def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k,
+                     causal: bool, scale: float):
+    """Sequences packed along a token axis, each attending only to itself.
+
+    q: [total_q, H, D], k and v: [total_k, H, D] float64; cu_q, cu_k: B+1
+    token offsets. Sequence b is query tokens cu_q[b] .. cu_q[b+1]-1 against
+    key tokens cu_k[b] .. cu_k[b+1]-1, each head the definition above (causal
+    masks aligned bottom-right within the sequence). Returns O [total_q, H, D]
+    and lse [H, total_q].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    total_q, H, D = q.shape
+    o = np.zeros((total_q, H, D))
+    lse = np.full((H, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        for h in range(H):
+            ob, lb = attention_rows(q[q0:q1, h], k[k0:k1, h], v[k0:k1, h],
+                                    np.arange(q1 - q0), causal, scale)
+            o[q0:q1, h] = ob
+            lse[h, q0:q1] = lb
+    return o, lse
 
 
 def attention_probs(q: np.ndarray, k: np.ndarray, causal: bool, scale: float):
@@ -127,22 +181,28 @@ def attention_probs(q: np.ndarray, k: np.ndarray, causal: bool, scale: float):
 def attention_bruteforce(q, k, v, causal: bool, scale: float):
     """Pure-Python loops with math.exp / math.log, for tiny single-head inputs.
 
-    q, k, v are sequences of rows (S x D). Follows the definition one scalar at
-    a time: logits, max, exponentials, sum, weighted sum of values, logsumexp.
+    q is a sequence of Sq rows, k and v of Sk rows (D values each). Follows
+    the definition one scalar at a time: logits, max, exponentials, sum,
+    weighted sum of values, logsumexp. A causal query i sees key j iff
+    j - i <= Sk - Sq; a query that sees no key gives a zero row and -inf.
     Returns (O as a list of rows, lse as a list).
     """
-    S = len(q)
+    Sq, Sk = len(q), len(k)
     D = len(q[0])
     O, LSE = [], []
-    for i in range(S):
+    for i in range(Sq):
         logits = []
-        for j in range(S):
-            if causal and j > i:
+        for j in range(Sk):
+            if causal and j - i > Sk - Sq:
                 continue
             dot = 0.0
             for d in range(D):
                 dot += float(q[i][d]) * float(k[j][d])
             logits.append((j, scale * dot))
+        if not logits:
+            O.append([0.0] * D)
+            LSE.append(-math.inf)
+            continue
         m = max(x for _, x in logits)
         w = [(j, math.exp(x - m)) for j, x in logits]
         l = sum(p for _, p in w)

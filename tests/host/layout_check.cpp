@@ -83,9 +83,11 @@ static std::vector<long> dma_tile(bool is_k, int* worst64) {
         const uint32_t dst = (is_k ? dma_lds_k<C>(w, i) : dma_lds_v<C>(w, i)) + 16 * p;
         const uint32_t src = is_k ? dma_src_k<C>(w, i, p) : dma_src_v<C>(w, i, p);
         // the kernel forms issue i's source offset as issue 0's plus a stride
-        CHECK(src == (is_k ? dma_src_k<C>(w, 0, p) + i * C::dmaStrideK
-                           : dma_src_v<C>(w, 0, p) + i * C::dmaStrideV),
-              "DMA source stride w=%d i=%d p=%d", w, i, p);
+        for (uint32_t rs = C::rowBytes; rs <= C::rowBytes + 48; rs += 16)
+          CHECK((is_k ? dma_src_k<C>(w, i, p, rs) : dma_src_v<C>(w, i, p, rs)) ==
+                    (is_k ? dma_src_k<C>(w, 0, p, rs) + i * (uint32_t)C::dmaRowsK * rs
+                          : dma_src_v<C>(w, 0, p, rs) + i * (uint32_t)C::dmaRowsV * rs),
+                "DMA source stride w=%d i=%d p=%d rs=%u", w, i, p, rs);
         addr[p] = dst;
         CHECK(dst % 16 == 0 && dst + 16 <= (uint32_t)C::tileBytes, "DMA dst %u", dst);
         CHECK(src % 16 == 0 && src + 16 <= (uint32_t)C::tileBytes, "DMA src %u", src);
@@ -187,19 +189,28 @@ static void check_lds() {
   CHECK(kw == 1 && vw == 1, "DMA writes conflict");
 }
 
+// Replays every global access of one kernel configuration for B*H heads
+// with Sq query rows and Sk key rows each (per-sequence lengths of a
+// variable-length batch are the same per work-group), rows `rs` bytes apart
+// in every tensor, and checks: the work-group map is a bijection; every key a
+// row sees lies in a tile its wave computes; tiles taken as mask-free hold
+// only keys every row of the wave sees; in-range rows stay inside their
+// buffer descriptors and rows past the end fall wholly outside; every O
+// element and lse entry is written exactly once.
 template <class C>
-static void check_global(int B, int H, int S, bool causal) {
+static void check_global(int B, int H, int Sq, int Sk, bool causal, uint32_t rs = C::rowBytes) {
   constexpr int D = C::D;
   const int BH = B * H;
-  const int nqt = num_q_tiles(S, C::BM);
+  const int nqt = num_q_tiles(Sq, C::BM);
   const long grid = (long)nqt * BH;
   constexpr int BN = C::BN;
-  const uint32_t head_bytes = (uint32_t)S * C::rowBytes;
+  const int off = Sk - Sq;
+  const uint32_t q_bytes = (uint32_t)Sq * rs;
   std::vector<char> seen(grid, 0);
-  const size_t head_elems = (size_t)S * D;
+  const size_t head_elems = (size_t)Sq * D;
   const bool track = head_elems * (size_t)BH <= ((size_t)1 << 26);
   std::vector<char> owritten(track ? head_elems * BH : 0, 0);
-  std::vector<char> lwritten(track ? (size_t)S * BH : 0, 0);
+  std::vector<char> lwritten(track ? (size_t)Sq * BH : 0, 0);
   for (long bid = 0; bid < grid; ++bid) {
     int qt, bh;
     block_to_tile((int)bid, BH, nqt, causal, &qt, &bh);
@@ -207,70 +218,84 @@ static void check_global(int B, int H, int S, bool causal) {
     const long cell = (long)qt * BH + bh;
     CHECK(!seen[cell], "tile visited twice");
     seen[cell] = 1;
-    const int kv_end = tile_kv_end(qt, S, causal, C::BM);
+    if (qt * C::BM >= Sq) continue;  // the work-group returns at once
+    const int kv_end = tile_kv_end(qt, Sq, Sk, causal, C::BM);
     const int ntiles = (kv_end + BN - 1) / BN;
-    CHECK(ntiles >= 1 && (ntiles - 1) * BN < S, "tile count");
+    CHECK(ntiles >= 0 && (ntiles == 0 || (ntiles - 1) * BN < Sk), "tile count");
     // DMA sources: tile-relative offsets; rows past the end start at or past
-    // the descriptor's range (S - kv0) * rowBytes
+    // the descriptor's range (Sk - kv0) * rs
     for (int t = 0; t < ntiles; ++t) {
-      const uint32_t range = (uint32_t)(S - t * BN) * C::rowBytes;
+      const uint32_t range = (uint32_t)(Sk - t * BN) * rs;
       for (int w = 0; w < C::NW; ++w)
         for (int i = 0; i < C::dmaPerWave; ++i)
           for (int p = 0; p < 64; ++p)
             for (int kv = 0; kv < 2; ++kv) {
-              const uint32_t off = kv ? dma_src_v<C>(w, i, p) : dma_src_k<C>(w, i, p);
-              const int row = off / C::rowBytes;
-              if (t * BN + row < S)
-                CHECK(off + 16 <= range, "DMA in-range row crosses the end");
+              const uint32_t o = kv ? dma_src_v<C>(w, i, p, rs) : dma_src_k<C>(w, i, p, rs);
+              const int row = o / rs;
+              CHECK(o % rs + 16 <= (uint32_t)C::rowBytes, "DMA chunk leaves its row");
+              if (t * BN + row < Sk)
+                CHECK(o + 16 <= range, "DMA in-range row crosses the end");
               else
-                CHECK(off >= range, "DMA row past S not wholly out of range");
+                CHECK(o >= range, "DMA row past Sk not wholly out of range");
             }
     }
     for (int wave = 0; wave < C::NW; ++wave) {
       for (int sub = 0; sub < C::RPW / kRowsPerWave; ++sub) {
       const int q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
-      const bool live = q0w < S;
-      const int nw = live ? (wave_kv_end(q0w, S, causal) + BN - 1) / BN : 0;
+      const bool live = q0w < Sq;
+      const int nw = live ? (wave_kv_end(q0w, Sq, Sk, causal) + BN - 1) / BN : 0;
       CHECK(nw <= ntiles, "wave computes a tile the work-group does not load");
+      if (live) {
+        const int unm = unmasked_tiles(q0w, Sq, Sk, causal, BN);
+        CHECK(unm <= nw, "mask-free tiles beyond the wave's tiles");
+        for (int r = q0w; r < q0w + kRowsPerWave && r < Sq; ++r) {
+          const int last = causal ? r + off : Sk - 1;  // last key row r sees
+          if (unm > 0)
+            CHECK(unm * BN - 1 <= last && unm * BN <= Sk, "tile %d taken as mask-free for row %d",
+                  unm - 1, r);
+        }
+      }
       for (int lane = 0; lane < 64; ++lane) {
         const int qrow = q0w + (lane & 31), hh = lane >> 5;
-        if (qrow < S) {
+        if (qrow < Sq) {
           // every key this row can see lies in a computed tile
-          const int last_key = causal ? qrow : S - 1;
-          CHECK(live && last_key < nw * BN, "row %d key %d not covered", qrow, last_key);
+          const int last_key = causal ? (qrow + off < Sk ? qrow + off : Sk - 1) : Sk - 1;
+          if (last_key >= 0)
+            CHECK(live && last_key < nw * BN, "row %d key %d not covered", qrow, last_key);
         }
         for (int j = 0; j < D / 16; ++j) {
-          const uint32_t off = q_frag_off<D>(qrow, j, hh);
-          if (qrow < S)
-            CHECK(off + 16 <= head_bytes, "Q load out of bounds");
+          const uint32_t o = q_frag_off<D>(qrow, j, hh, rs);
+          if (qrow < Sq)
+            CHECK(o + 16 <= q_bytes, "Q load out of bounds");
           else
-            CHECK(off >= head_bytes, "Q row past S not wholly out of range");
+            CHECK(o >= q_bytes, "Q row past Sq not wholly out of range");
         }
         if (!live) continue;
         for (int jd = 0; jd < D / 32; ++jd)
           for (int g = 0; g < 2; ++g) {
-            const uint32_t off = o_frag_off<D>(qrow, jd, g, hh);
-            if (qrow >= S) {
-              CHECK(off >= head_bytes, "O store past S not wholly out of range");
+            const uint32_t o = o_frag_off<D>(qrow, jd, g, hh, rs);
+            if (qrow >= Sq) {
+              CHECK(o >= q_bytes, "O store past Sq not wholly out of range");
               continue;
             }
-            CHECK(off + 16 <= head_bytes, "O store out of bounds");
+            CHECK(o + 16 <= q_bytes && o % rs + 16 <= (uint32_t)C::rowBytes,
+                  "O store out of bounds");
             if (track)
               for (int e = 0; e < 8; ++e) {
-                const size_t p = (size_t)bh * head_elems + off / 2 + e;
-                CHECK(!owritten[p], "O element written twice");
-                owritten[p] = 1;
+                const size_t pe = (size_t)bh * head_elems + (size_t)(o / rs) * D + (o % rs) / 2 + e;
+                CHECK(!owritten[pe], "O element written twice");
+                owritten[pe] = 1;
               }
           }
         if (hh == 0) {
-          if (qrow < S) {
-            CHECK((uint32_t)qrow * 4u + 4u <= (uint32_t)S * 4u, "lse store");
+          if (qrow < Sq) {
+            CHECK((uint32_t)qrow * 4u + 4u <= (uint32_t)Sq * 4u, "lse store");
             if (track) {
-              CHECK(!lwritten[(size_t)bh * S + qrow], "lse written twice");
-              lwritten[(size_t)bh * S + qrow] = 1;
+              CHECK(!lwritten[(size_t)bh * Sq + qrow], "lse written twice");
+              lwritten[(size_t)bh * Sq + qrow] = 1;
             }
           } else {
-            CHECK((uint32_t)qrow * 4u >= (uint32_t)S * 4u, "lse past S in range");
+            CHECK((uint32_t)qrow * 4u >= (uint32_t)Sq * 4u, "lse past Sq in range");
           }
         }
       }
@@ -282,6 +307,22 @@ static void check_global(int B, int H, int S, bool causal) {
     for (size_t p = 0; p < owritten.size(); ++p) CHECK(owritten[p], "O element not written");
     for (size_t p = 0; p < lwritten.size(); ++p) CHECK(lwritten[p], "lse not written");
   }
+}
+
+template <class C> static void check_global(int B, int H, int S, bool causal) {
+  check_global<C>(B, H, S, S, causal);
+}
+
+// Query/key length pairs (as in a variable-length batch), with padded rows.
+template <class C> static void check_lengths() {
+  const int lens[] = {0, 1, 31, 32, 33, 95, 96, 97, 200, 255, 256, 257, 513};
+  for (int lq : lens)
+    for (int lk : lens)
+      for (int causal = 0; causal < 2; ++causal) {
+        if (lq == 0) continue;
+        check_global<C>(1, 2, lq, lk, causal != 0);
+        check_global<C>(1, 1, lq, lk, causal != 0, C::rowBytes + 48);
+      }
 }
 
 // ------------------------------------------------ ping-pong schedule replay
@@ -478,6 +519,13 @@ int main() {
       check_global<CfgW2<64>>(s[0], s[1], s[2], causal);
       check_global<CfgW2<128>>(s[0], s[1], s[2], causal);
     }
+  check_lengths<Cfg4<64>>();
+  check_lengths<Cfg4<128>>();
+  check_lengths<Cfg8<64>>();
+  check_lengths<Cfg8<128>>();
+  check_lengths<CfgW2<64>>();
+  check_lengths<CfgW2<128>>();
+  std::printf("query/key length pairs (bottom-right causal), padded rows: checked\n");
   // full-size shapes (O coverage tracked up to 64M elements)
   check_global<Cfg4<64>>(1, 16, 1024, true);
   check_global<Cfg8<64>>(10, 64, 1024, false);

@@ -13,7 +13,7 @@ from exact_attention_16_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
 
-OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG, LAYOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 def _declared():
@@ -24,7 +24,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == {"fa_fwd", "fa_fwd_f16", "fa_fwd_bf16", "fa_fwd_diag",
-                           "fa_fwd_tile", "fa_strerror", "fa_version"}
+                           "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_tile", "fa_strerror",
+                           "fa_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -53,8 +54,8 @@ def test_kernel_launch_stubs_are_defined():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 200
-    for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG):
+    assert fa.fa_version() == 300
+    for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG, LAYOUT):
         assert fa.fa_strerror(st) and fa.fa_strerror(st) != "unknown status"
     assert fa.fa_strerror(12345) == "unknown status"
 
@@ -150,3 +151,90 @@ def test_kernel_index_math_on_host(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     print(r.stdout)
     assert r.returncode == 0 and r.stdout.strip().endswith("OK"), r.stdout
+
+
+# ------------------------------------------------ strided and variable-length
+B_, H_, SQ, SK, D_ = 2, 3, 100, 80, 64
+
+
+def _dense(B, H, Sq, Sk, D):
+    """14 strides of contiguous [B,H,S,D] q/k/v/o and [B,H,Sq] lse."""
+    q = [H * Sq * D, Sq * D, D]
+    k = [H * Sk * D, Sk * D, D]
+    return q + k + k + q + [H * Sq, Sq]
+
+
+def _strided(strides=None, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=B_, H=H_, Sq=SQ, Sk=SK, D=D_, causal=1, scale=0.125,
+             dtype=0)
+    a.update(kw)
+    st = _dense(B_, H_, SQ, SK, D_) if strides is None else strides
+    return fa.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"],
+                             a["Sk"], a["D"], a["causal"], a["scale"], None, a["dtype"], st,
+                             check=False)
+
+
+def _with(i, x):
+    st = _dense(B_, H_, SQ, SK, D_)
+    st[i] = x
+    return st
+
+
+@pytest.mark.parametrize("strides,kw,expect", [
+    (None, dict(q=0), NULL), (None, dict(lse=0), NULL),
+    (None, dict(Sq=-1), DIM), (None, dict(Sk=-1), DIM), (None, dict(D=80), UNSUP),
+    (None, dict(scale=0.0), SCALE), (None, dict(causal=3), ARG),
+    (_with(2, -64), {}, LAYOUT),            # negative row stride
+    (_with(5, 32), {}, LAYOUT),             # k rows shorter than D
+    (_with(11, 8), {}, LAYOUT),             # o rows overlap each other
+    (_with(10, 64), {}, LAYOUT),            # o heads overlap (head stride one row)
+    (_with(13, 1), {}, LAYOUT),             # lse heads overlap
+    (_with(2, 68), {}, ALIGN),              # q rows not 16-byte aligned
+    (_with(7, 64 * 3 + 4), {}, ALIGN),      # v heads not 16-byte aligned
+    (_with(11, 1 << 24), {}, DIM),          # 32-bit offsets within one head
+    (None, dict(o=K + 4096), ALIAS),        # o inside k's span
+    (None, dict(lse=O + 64), ALIAS),
+])
+def test_strided_validation(strides, kw, expect):
+    assert _strided(strides, **kw) == expect
+
+
+def test_strided_needs_strides_and_empty_is_a_noop():
+    assert _lib.load().fa_fwd_strided(Q, K, V, O, L, 1, 1, 8, 8, 64, 0, 0.1, None, 0,
+                                      None) == NULL
+    assert _strided(Sq=0) == OK
+    assert _strided(B=0) == OK
+    assert _lib.load().fa_fwd_strided(0, 0, 0, 0, 0, 1, 1, 0, 8, 64, 0, 0.1, None, 0, None) == OK
+
+
+def _varlen_call(cu_q=0x30000000000, cu_k=0x30000001000, total_q=50, total_k=60, strides=None,
+                 **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=4, H=2, mq=20, mk=30, D=64, causal=1, scale=0.125,
+             dtype=1)
+    a.update(kw)
+    # packed [total, H, D]: head stride D, row stride H*D; lse [H, total_q]
+    st = [64, 128, 64, 128, 64, 128, 64, 128, total_q] if strides is None else strides
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], cu_q, cu_k, a["B"], a["H"],
+                            a["mq"], a["mk"], total_q, total_k, a["D"], a["causal"], a["scale"],
+                            None, a["dtype"], st, check=False)
+
+
+# (inputs may overlap themselves: they are read only; only outputs are checked)
+@pytest.mark.parametrize("args,expect", [
+    (dict(cu_q=0), NULL), (dict(cu_k=0), NULL), (dict(cu_q=0x30000000002), ALIGN),
+    (dict(total_q=-1), DIM), (dict(total_k=-1), DIM), (dict(B=-1), DIM),
+    (dict(D=32), UNSUP), (dict(scale=-1.0), SCALE), (dict(causal=5), ARG),
+    (dict(q=0), NULL),
+    (dict(strides=[64, 128, 64, 128, 64, 128, 64, 64, 50]), LAYOUT),   # o rows overlap
+    (dict(strides=[64, 128, 64, 128, 64, 128, 64, 128, 10]), LAYOUT),  # lse heads overlap
+    (dict(strides=[64, 132, 64, 128, 64, 128, 64, 128, 50]), ALIGN),
+    (dict(o=V + 256), ALIAS),
+])
+def test_varlen_validation(args, expect):
+    assert _varlen_call(**args) == expect
+
+
+@pytest.mark.parametrize("args", [dict(total_q=0), dict(B=0), dict(mq=0),
+                                  dict(total_q=0, cu_q=0, cu_k=0, q=0)])
+def test_varlen_empty_is_a_noop(args):
+    assert _varlen_call(**args) == OK

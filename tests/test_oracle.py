@@ -227,11 +227,15 @@ def test_online_threshold_reduces_rescales():
 def _pin_battery():
     """Brute force, closed forms and the overflow case; True if all pass."""
     try:
-        for S, D, causal in ((8, 4, False), (8, 4, True), (5, 3, True)):
-            q, k, v = _rand((S, D), 40 + S), _rand((S, D), 50 + S), _rand((S, D), 60 + S)
+        for Sq, Sk, D, causal in ((8, 8, 4, False), (8, 8, 4, True), (5, 5, 3, True),
+                                  (5, 8, 3, True), (8, 5, 3, True), (3, 7, 2, False)):
+            q, k, v = _rand((Sq, D), 40 + Sq), _rand((Sk, D), 50 + Sk), _rand((Sk, D), 60 + Sk)
             o, lse = oracle.attention_fwd(q, k, v, causal, 0.6)
             ob, lb = oracle.attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), causal, 0.6)
-            if not (np.allclose(o, ob, atol=1e-12, rtol=0) and np.allclose(lse, lb, atol=1e-12, rtol=0)):
+            if not (np.allclose(o, ob, atol=1e-12, rtol=0)
+                    and np.array_equal(np.isinf(lse), np.isinf(lb))
+                    and np.allclose(np.nan_to_num(lse, neginf=0), np.nan_to_num(np.array(lb), neginf=0),
+                                    atol=1e-12, rtol=0)):
                 return False
         for case in _golden_cases():
             for causal in (False, True):
@@ -258,10 +262,14 @@ def _pin_battery():
 _MUTANTS = {
     "K and Q swapped in the logits": ("_logits", lambda q, k, scale: scale * (k @ q.T)),
     "scale dropped": ("_logits", lambda q, k, scale: q @ k.T),
-    "mask hides the diagonal": ("_causal_mask", lambda x, rows: np.where(
-        np.arange(x.shape[1])[None, :] >= rows[:, None], -np.inf, x)),
-    "mask keeps the upper triangle": ("_causal_mask", lambda x, rows: np.where(
-        np.arange(x.shape[1])[None, :] < rows[:, None], -np.inf, x)),
+    "mask hides the diagonal": ("_causal_mask", lambda x, rows, offset=0: np.where(
+        np.arange(x.shape[1])[None, :] >= rows[:, None] + offset, -np.inf, x)),
+    "mask keeps the upper triangle": ("_causal_mask", lambda x, rows, offset=0: np.where(
+        np.arange(x.shape[1])[None, :] < rows[:, None] + offset, -np.inf, x)),
+    "mask alignment offset ignored": ("_causal_mask", lambda x, rows, offset=0: np.where(
+        np.arange(x.shape[1])[None, :] > rows[:, None], -np.inf, x)),
+    "mask alignment offset negated": ("_causal_mask", lambda x, rows, offset=0: np.where(
+        np.arange(x.shape[1])[None, :] > rows[:, None] - offset, -np.inf, x)),
     "max over the wrong axis": ("_row_max", lambda x: x.max(axis=0)),
     "max subtraction dropped": ("_row_max", lambda x: np.zeros(x.shape[0])),
     "exponent sign flipped": ("_exp_shifted", lambda x, m: np.exp(-(x - m[:, None]))),
@@ -283,3 +291,93 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = _MUTANTS[name]
     monkeypatch.setattr(OA, attr, fn)
     assert not _pin_battery(), f"planted mistake not caught: {name}"
+
+
+# ------------------------------------- query and key lengths that differ; varlen
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 5), (3, 8), (8, 3), (5, 1), (7, 7), (4, 9)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_lengths_match_bruteforce(Sq, Sk, causal):
+    """Scalar loops (key j visible iff j - i <= Sk - Sq) against the vectorised oracle."""
+    D = 4
+    q, k, v = _rand((Sq, D), 300 + Sq), _rand((Sk, D), 310 + Sk), _rand((Sk, D), 320 + Sk)
+    o, lse = oracle.attention_fwd(q, k, v, causal, 0.7)
+    ob, lb = oracle.attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), causal, 0.7)
+    np.testing.assert_allclose(o, ob, atol=1e-12, rtol=0)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(np.array(lb)))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(lse[fin], np.array(lb)[fin], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("S,Sq", [(40, 1), (40, 13), (129, 64)])
+def test_bottom_right_is_the_end_of_a_square_causal_problem(S, Sq):
+    """Invariant: the last Sq queries of a square causal problem over S keys give the
+    same rows as those Sq queries alone against all S keys (bottom-right mask)."""
+    D = 16
+    q, k, v = _rand((S, D), 330), _rand((S, D), 331), _rand((S, D), 332)
+    o_full, l_full = oracle.attention_fwd(q, k, v, True, D ** -0.5)
+    o, l = oracle.attention_fwd(q[S - Sq:], k, v, True, D ** -0.5)
+    np.testing.assert_allclose(o, o_full[S - Sq:], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(l, l_full[S - Sq:], atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("Sq,Sk", [(64, 96), (96, 64), (33, 200)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_lengths_match_torch_sdpa_with_explicit_mask(Sq, Sk, causal):
+    """Library pin: torch's scaled_dot_product_attention (CPU, float64) with the
+    bottom-right mask given explicitly, on the rows that see at least one key."""
+    D = 32
+    q, k, v = _rand((Sq, D), 340), _rand((Sk, D), 341), _rand((Sk, D), 342)
+    o, lse = oracle.attention_fwd(q, k, v, causal, D ** -0.5)
+    mask = torch.ones(Sq, Sk, dtype=torch.bool)
+    if causal:
+        mask = mask.tril(diagonal=Sk - Sq)
+    seen = mask.any(dim=1).numpy()
+    t = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=mask[None], scale=D ** -0.5)[0].numpy()
+    np.testing.assert_allclose(o[seen], t[seen], atol=1e-12, rtol=0)
+    ref_lse = np.logaddexp.reduce(np.where(mask.numpy(), (q @ k.T) * D ** -0.5, -np.inf), axis=1)
+    np.testing.assert_allclose(lse[seen], ref_lse[seen], atol=1e-12, rtol=0)
+
+
+def test_rows_that_see_no_key():
+    """Reading: a causal query with no visible key (Sk < Sq, its first Sq - Sk
+    rows) returns a zero row and lse = -inf; with Sk = 0 every row does."""
+    q, k, v = _rand((6, 3), 350), _rand((2, 3), 351), _rand((2, 3), 352)
+    o, lse = oracle.attention_fwd(q, k, v, True, 1.0)
+    assert np.all(o[:4] == 0) and np.all(np.isneginf(lse[:4]))
+    assert np.all(np.isfinite(lse[4:]))
+    o0, l0 = oracle.attention_fwd(q, np.zeros((0, 3)), np.zeros((0, 3)), False, 1.0)
+    assert np.all(o0 == 0) and np.all(np.isneginf(l0))
+
+
+def test_varlen_of_equal_lengths_is_the_batch():
+    """Packing a [B, H, S, D] batch along the token axis with offsets 0, S, 2S, ...
+    gives attention_fwd's result, rearranged."""
+    B, H, S, D = 3, 2, 20, 8
+    q, k, v = _rand((B, H, S, D), 360), _rand((B, H, S, D), 361), _rand((B, H, S, D), 362)
+    cu = np.arange(B + 1) * S
+    pack = lambda t: t.transpose(0, 2, 1, 3).reshape(B * S, H, D)
+    for causal in (False, True):
+        o, lse = oracle.attention_fwd(q, k, v, causal, 0.3)
+        ov, lv = oracle.attention_varlen(pack(q), pack(k), pack(v), cu, cu, causal, 0.3)
+        np.testing.assert_allclose(ov, pack(o), atol=1e-14, rtol=0)
+        np.testing.assert_allclose(lv, lse.transpose(1, 0, 2).reshape(H, B * S), atol=1e-14, rtol=0)
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    """Each sequence equals a separate call on its own rows; empty sequences and
+    Sq != Sk per sequence included."""
+    H, D = 2, 8
+    lq, lk = [5, 0, 17, 3, 9], [5, 4, 17, 8, 2]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q, k, v = _rand((cq[-1], H, D), 370), _rand((ck[-1], H, D), 371), _rand((ck[-1], H, D), 372)
+    for causal in (False, True):
+        o, lse = oracle.attention_varlen(q, k, v, cq, ck, causal, 0.4)
+        for b in range(len(lq)):
+            qs, ks = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+            for h in range(H):
+                ob, lb = oracle.attention_fwd(q[qs, h], k[ks, h], v[ks, h], causal, 0.4)
+                np.testing.assert_array_equal(o[qs, h], ob)
+                np.testing.assert_array_equal(lse[h, qs], lb)

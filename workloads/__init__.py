@@ -143,3 +143,51 @@ def random_bits(shape, dtype: str, seed: int, mean: float = 0.0, std: float = 1.
     x = (mean + std * rng.standard_normal(shape)).astype(np.float32)
     return round_bits(x, dtype)
 
+
+
+# Variable-length batch: sequences of different lengths packed along a token
+# axis ([total, H, D]), the situation of the dynamic-shape section (6.3) of
+# the xdnf.cn page (lengths that vary per request). Lengths are drawn
+# uniformly from [lo, hi] with their own seed; Q, K, V are N(0,1) like the
+# fixed-length workloads.
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    B: int
+    H: int
+    D: int
+    lo: int
+    hi: int
+    dtype: str
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.D)))
+
+    def lengths(self) -> np.ndarray:
+        rng = np.random.default_rng(self.seed)
+        return rng.integers(self.lo, self.hi + 1, size=self.B).astype(np.int64)
+
+    def flops(self) -> float:
+        """Metric convention per sequence: 4*H*L^2*D, halved when causal."""
+        L = self.lengths().astype(np.float64)
+        f = 4.0 * self.H * float((L * L).sum()) * self.D
+        return f / 2 if self.causal else f
+
+
+VARLEN = VarlenWorkload("varlen", B=16, H=16, D=128, lo=256, hi=8192, dtype=BF16, causal=True,
+                        seed=8)
+
+
+def make_varlen_inputs(w: VarlenWorkload):
+    """Token offsets (B+1, int32) and Q, K, V bits of shape (total, H, D)."""
+    L = w.lengths()
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    rng = np.random.default_rng(w.seed + 1)
+    shape = (int(cu[-1]), w.H, w.D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    return cu, round_bits(q, w.dtype), round_bits(k, w.dtype), round_bits(v, w.dtype)
