@@ -13,6 +13,9 @@ Contents:
   float64, materialising the full score matrix (also for query and key
   lengths that differ and for sequences packed along a token axis), plus a
   pure-Python brute force for tiny inputs.
+* :mod:`oracle.fp8` -- exact attention of 8-bit float (E4M3) inputs with
+  per-tensor descales, and the bound on how far rounding the probabilities
+  to E4M3 before the P V product can move O.
 * :mod:`oracle.online` -- the streaming (tiled, online-softmax) algorithm with
   the lagging-max conditional rescale, in float64, step by step in the pages'
   order. It is used to check that the lagging-max algebra reaches the plain
@@ -20,7 +23,9 @@ Contents:
 """
 from .attention import (attention_fwd, attention_rows, attention_probs,
                         attention_bruteforce, attention_varlen)
+from .fp8 import attention_fp8, attention_fp8_rows, pv_rounding_bound
 from .online import online_softmax_attention
 
 __all__ = ["attention_fwd", "attention_rows", "attention_probs",
-           "attention_bruteforce", "attention_varlen", "online_softmax_attention"]
+           "attention_bruteforce", "attention_varlen", "online_softmax_attention",
+           "attention_fp8", "attention_fp8_rows", "pv_rounding_bound"]

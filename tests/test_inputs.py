@@ -85,3 +85,66 @@ def test_workload_table():
     assert W.WORKLOADS["bat"].flops == 171_798_691_840
     assert W.WORKLOADS["dec"].algorithmic_bytes == 8_454_144
     assert W.WORKLOADS["tiny"].scale == np.float32(0.125)
+
+
+# ---- 8-bit float E4M3FN (OCP 8-bit floating point specification) ----------
+
+def test_e4m3_decode_known_codes():
+    # exponent bias 7, three mantissa bits, no infinities, S.1111.111 is NaN
+    codes = np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x39, 0x3F, 0x40, 0x7E, 0xB8, 0xFE])
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.125, 1.875, 2.0, 448.0,
+            -1.0, -448.0]
+    got = W.decode(codes, W.E4M3)
+    np.testing.assert_array_equal(got, want)
+    assert np.signbit(got[1]) and not np.signbit(got[0])
+    assert np.isnan(W.decode(np.array([0x7F, 0xFF]), W.E4M3)).all()
+
+
+def test_e4m3_codes_are_monotone_and_spaced():
+    v = W.decode(np.arange(0x7F), W.E4M3)
+    d = np.diff(v)
+    assert (d > 0).all()
+    # spacing 2^-9 through the subnormals and the first binade, then doubles per binade
+    assert (d[:15] == 2.0 ** -9).all()
+    for e in range(1, 16):
+        assert (d[8 * e: 8 * e + 7] == 2.0 ** (e - 10)).all()
+
+
+def test_e4m3_round_trip_all_finite_codes():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = W.decode(codes, W.E4M3)
+    np.testing.assert_array_equal(W.f32_to_e4m3_bits(vals.astype(np.float32)), codes)
+
+
+def test_e4m3_ties_to_even_and_saturation():
+    x = np.array([1.0625, 1.1875, 3 * 2.0 ** -10, 2.0 ** -10, 464.0, 500.0, 1e30, -1e30, np.nan])
+    np.testing.assert_array_equal(W.f32_to_e4m3_bits(x),
+                                  [0x38, 0x3A, 0x02, 0x00, 0x7E, 0x7E, 0x7E, 0xFE, 0x7F])
+
+
+def test_e4m3_rounding_matches_torch_in_range():
+    x = _edge_f32()
+    x = np.concatenate([x / 64, x * 16, x / 4096])
+    x = x[np.abs(x) <= 448]
+    ours = W.f32_to_e4m3_bits(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_fp8_inputs_span_the_range_and_round_to_nearest():
+    w = W.Workload("t8", 1, 2, 256, 128, W.E4M3, True, 9)
+    (qc, kc, vc), ds = W.make_fp8_inputs(w)
+    rng = np.random.default_rng(9)
+    xs = [rng.standard_normal((1, 2, 256, 128), dtype=np.float32) for _ in range(3)]
+    for c, d, x in zip((qc, kc, vc), ds, xs):
+        assert c.dtype == np.uint8 and c.shape == x.shape
+        assert d == float(np.float32(np.abs(x).max() / 448))
+        val = W.decode(c, W.E4M3)
+        assert np.abs(val).max() == 448.0  # the largest magnitude maps to 448
+        # each code is a nearest E4M3 value of x / d: within half a spacing
+        y = x.astype(np.float64) / d
+        err = np.abs(val - y)
+        _, e = np.frexp(np.abs(y))
+        half = np.where(e - 1 >= -6, np.ldexp(1.0, e - 5), 2.0 ** -10)
+        assert (err <= half * (1 + 1e-12)).all()
+    assert W.WORKLOADS["long8"].algorithmic_bytes == 5 * 2 * 16 * 8192 * 128 + 4 * 2 * 16 * 8192

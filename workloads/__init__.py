@@ -18,6 +18,8 @@ bat   10, 64, 1024, 64                  fp16   no      the Triton FA2 study's sh
                                                        的Triton性能考古学", grid section)
 long  2, 16, 8192, 128                  bf16   yes     long-context causal
 ramp  1, 8, 16384, 128                  bf16   yes     rescale stress (key ramp)
+long8 2, 16, 8192, 128                  e4m3   yes     the long workload in 8-bit
+                                                       floats, per-tensor scales
 ====  ================================  =====  ======  ==========================
 
 Recipe: ``numpy.random.default_rng(seed)`` draws Q, then K, then V as float32
@@ -26,6 +28,11 @@ Recipe: ``numpy.random.default_rng(seed)`` draws Q, then K, then V as float32
 every query row, summed in float32.  Rounding to fp16 is numpy's
 round-to-nearest-even ``astype``; rounding to bf16 is the bit-exact
 round-to-nearest-even of the float32 pattern.
+
+8-bit inputs (``make_fp8_inputs``): the same float32 draws, then per tensor a
+descale d = float32(max|x| / 448) and codes E4M3(x / d) (nearest, ties to
+even), so that each tensor spans E4M3's range; the value of a code is
+decode(code) * d.
 """
 from __future__ import annotations
 
@@ -36,9 +43,12 @@ import numpy as np
 
 F16 = "f16"
 BF16 = "bf16"
+E4M3 = "e4m3"  # OCP 8-bit float E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits,
+               # no infinities, S.1111.111 = NaN, largest finite 448
 
 # numeric codes shared with the C ABI's dtype enum (FA_F16 = 0, FA_BF16 = 1)
 DTYPE_CODE = {F16: 0, BF16: 1}
+ELEM_BYTES = {F16: 2, BF16: 2, E4M3: 1}
 
 
 @dataclass(frozen=True)
@@ -66,9 +76,9 @@ class Workload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """Q, K, V read once and O written once (2 B/element) + LSE (4 B/row)."""
+        """Q, K, V read once (their element size), O written once (16-bit), LSE (4 B/row)."""
         n = self.B * self.H * self.S * self.D
-        return 4 * 2 * n + 4 * self.B * self.H * self.S
+        return (3 * ELEM_BYTES[self.dtype] + 2) * n + 4 * self.B * self.H * self.S
 
     def with_causal(self, causal: bool) -> "Workload":
         return Workload(self.name, self.B, self.H, self.S, self.D, self.dtype,
@@ -82,6 +92,7 @@ WORKLOADS = {
     "bat": Workload("bat", 10, 64, 1024, 64, F16, False, 3),
     "long": Workload("long", 2, 16, 8192, 128, BF16, True, 4),
     "ramp": Workload("ramp", 1, 8, 16384, 128, BF16, True, 5, ramp=0.002),
+    "long8": Workload("long8", 2, 16, 8192, 128, E4M3, True, 4),
 }
 
 
@@ -102,16 +113,45 @@ def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
+def _e4m3_table() -> np.ndarray:
+    """Values of the finite non-negative E4M3FN codes 0x00 .. 0x7E, ascending."""
+    c = np.arange(0x7F, dtype=np.int64)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e - 10))
+
+
+_E4M3 = _e4m3_table()
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to E4M3FN (nearest, ties to even), saturating at +-448; uint8 bits."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3, a), 1, len(_E4M3) - 1)  # first code >= a
+    lo = hi - 1
+    dlo, dhi = a - _E4M3[lo], _E4M3[hi] - a
+    code = np.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(a <= _E4M3[0], 0, code)
+    out = code | np.where(np.signbit(x), 0x80, 0)
+    return np.where(np.isnan(x), 0x7F, out).astype(np.uint8)
+
+
 def round_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == F16:
         return f32_to_f16_bits(x)
     if dtype == BF16:
         return f32_to_bf16_bits(x)
+    if dtype == E4M3:
+        return f32_to_e4m3_bits(x)
     raise ValueError(dtype)
 
 
 def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 values of 16-bit storage."""
+    """Exact float64 values of 16-bit (or, for E4M3, 8-bit) storage."""
+    if dtype == E4M3:
+        b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+        mag = np.where((b & 0x7F) == 0x7F, np.nan, _E4M3[np.minimum(b & 0x7F, 0x7E)])
+        return np.where(b & 0x80, -mag, mag)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == F16:
         return bits.view(np.float16).astype(np.float64)
@@ -135,6 +175,22 @@ def make_inputs(w: Workload, ramp_override: float | None = None):
         k += (ramp * j[:, None] * u[None, :]).astype(np.float32)
         q += u.astype(np.float32)
     return (round_bits(q, w.dtype), round_bits(k, w.dtype), round_bits(v, w.dtype))
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor scaled E4M3: (codes, descale) with descale = float32(max|x| / 448)."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    d = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    return f32_to_e4m3_bits(np.asarray(x, dtype=np.float64) / d), d
+
+
+def make_fp8_inputs(w: Workload):
+    """Seeded Q, K, V as E4M3 codes (uint8, (B, H, S, D)) and their descales (dq, dk, dv)."""
+    rng = np.random.default_rng(w.seed)
+    shape = (w.B, w.H, w.S, w.D)
+    xs = [rng.standard_normal(shape, dtype=np.float32) for _ in range(3)]
+    out = [quantize_e4m3(x) for x in xs]
+    return tuple(c for c, _ in out), tuple(d for _, d in out)
 
 
 def random_bits(shape, dtype: str, seed: int, mean: float = 0.0, std: float = 1.0):
