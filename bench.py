@@ -13,6 +13,11 @@ Default workload: B=2, H=16, S=8192, D=128, bf16, causal (the long-context
 configuration the metric is quoted on). FLOPs follow the metric:
 4*B*H*S^2*D, halved when causal.
 
+--workload long8 times the 8-bit entry point (fa_fwd_fp8) on the same shape
+with E4M3 inputs and per-tensor descales, against the fp8 MFMA peak, and
+prints its own JSON line (its CPU baseline is the same oracle on the decoded
+values).
+
 --varlen times the variable-length entry point instead, on a packed batch of
 16 causal sequences with seeded lengths in [256, 8192] (H=16, D=128, bf16),
 and prints its own JSON line; FLOPs then sum the metric over the sequences.
@@ -43,9 +48,10 @@ import workloads as W  # noqa: E402
 
 METRIC = "attention fwd TFLOPS (B·H·S²·D·4, causal halved) + % of bf16 MFMA peak"
 PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA peak (published 2.5 PFLOP/s)
+PEAK_TFLOPS_FP8 = 5033.2  # MI355X dense fp8 MFMA peak (published 5.0 PFLOP/s)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_layout.h")]
+                  for f in ("fa_fwd.hip", "fa_layout.h", "fa_device.h", "fa_pingpong.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_long_hbm_traffic.json")
 
 
@@ -147,7 +153,7 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def cpu_baseline(w: W.Workload, qb, kb, vb, budget_s: float = 15.0):
+def cpu_baseline(w: W.Workload, qb, kb, vb, budget_s: float = 15.0, descale=(1.0, 1.0, 1.0)):
     """The float64 oracle on a random sample of query rows of the workload.
 
     Rows are drawn uniformly over all heads and positions, processed in
@@ -168,9 +174,9 @@ def cpu_baseline(w: W.Workload, qb, kb, vb, budget_s: float = 15.0):
         i += 1
         b, h = divmod(bh, w.H)
         rows = np.sort(rng.choice(w.S, size=batch, replace=False))
-        q = W.decode(qb[b, h], w.dtype)
-        k = W.decode(kb[b, h], w.dtype)
-        v = W.decode(vb[b, h], w.dtype)
+        q = W.decode(qb[b, h], w.dtype) * descale[0]
+        k = W.decode(kb[b, h], w.dtype) * descale[1]
+        v = W.decode(vb[b, h], w.dtype) * descale[2]
         oracle.attention_rows(q, k, v, rows, w.causal, w.scale)
         done += batch
     dt = time.perf_counter() - t0
@@ -212,6 +218,8 @@ def main(argv=None) -> int:
     if args.varlen:
         return bench_varlen(args, torch, fa)
     w = W.WORKLOADS[args.workload]
+    if w.dtype == W.E4M3:
+        return bench_fp8(args, torch, fa, w)
     dev = torch.device("cuda:0")
     fa.load()  # fails loudly if the HIP library is not built
     qb, kb, vb = W.make_inputs(w)
@@ -299,6 +307,81 @@ def main(argv=None) -> int:
                    "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
                    "parallelism": "single GPU"},
         "pct_of_peak": 100 * tflops / PEAK_TFLOPS,
+        "wall_s": wall,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def timed(step, stream, torch, steps: int, warmup: int):
+    """W untimed steps, then K timed back-to-back on `stream` (HIP events on
+    that stream); returns (ms per step, wall seconds, median single-launch ms)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * min(steps, 20))]
+    for i in range(0, len(evs), 2):
+        evs[i].record(stream)
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    med = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]))
+    return ms, wall, med
+
+
+def bench_fp8(args, torch, fa, w) -> int:
+    """Time fa_fwd_fp8 on the 8-bit workload; one JSON line."""
+    dev = torch.device("cuda:0")
+    fa.load()
+    (qc, kc, vc), ds = W.make_fp8_inputs(w)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (qc, kc, vc))
+    o = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        fa.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      w.B, w.H, w.S, w.D, int(w.causal), w.scale, ds[0], ds[1], ds[2],
+                      stream.cuda_stream)
+
+    torch.cuda.synchronize()
+    ms, wall, med = timed(step, stream, torch, args.steps, args.warmup)
+    assert bool(torch.isfinite(lse).all()), "non-finite output"
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    print(f"Average Time Per Step:     {ms:.4f} ms\n"
+          f"Compute Performance:       {tflops:.2f} TFLOPS ({100 * tflops / PEAK_TFLOPS_FP8:.1f}% "
+          f"of {PEAK_TFLOPS_FP8} fp8 peak)\n"
+          f"Median single launch:      {med:.4f} ms", file=sys.stderr, flush=True)
+    groups = w.B * w.H * -(-w.S // 256)
+    roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS_FP8, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_TFLOPS_FP8, "traffic": None,
+                "kernel": f"fa_fwd_pp8<causal={int(w.causal)}> ({groups} work-groups x 512 "
+                          f"threads, 256 query rows, 128-key tiles)",
+                "flops_per_launch": w.flops, "avg_launch_ms": ms, "median_launch_ms": med,
+                "algorithmic_bytes_per_launch": w.algorithmic_bytes}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, qc, kc, vc, descale=ds)
+    out = {
+        "metric": "attention fwd TFLOPS (B·H·S²·D·4, causal halved) + % of fp8 MFMA peak",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic: seeded N(0,1) Q/K/V, per-tensor scaled to E4M3",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} S={w.S} D={w.D} e4m3 inputs, bf16 "
+                               f"output, {'causal' if w.causal else 'non-causal'}",
+                   "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
+                   "descales": list(ds), "parallelism": "single GPU"},
+        "pct_of_peak": 100 * tflops / PEAK_TFLOPS_FP8,
         "wall_s": wall,
         "roofline": roofline,
         "cpu_baseline": cpu,

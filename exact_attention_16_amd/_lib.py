@@ -44,6 +44,7 @@ SIGNATURES = {
     "fa_fwd_diag": (_I, _FWD_ARGS + [_I, _I, _I, _P]),
     "fa_fwd_strided": (_I, [_P] * 5 + [_I] * 6 + [_F, _P, _I, _P]),
     "fa_fwd_varlen": (_I, [_P] * 7 + [_I] * 8 + [_F, _P, _I, _P]),
+    "fa_fwd_fp8": (_I, [_P] * 5 + [_I] * 5 + [_F] * 4 + [_P]),
     "fa_fwd_tile": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
                          ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_longlong)]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
@@ -127,6 +128,13 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_
                               max_seqlen_k, total_q, total_k, D, int(causal), scale, stream,
                               dtype, _strides(strides, 9))
     return _check(st, "fa_fwd_varlen") if check else st
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, S, D, causal, scale, descale_q, descale_k, descale_v,
+               stream, check=True):
+    st = load().fa_fwd_fp8(q, k, v, o, lse, B, H, S, D, int(causal), scale, descale_q,
+                           descale_k, descale_v, stream)
+    return _check(st, "fa_fwd_fp8") if check else st
 
 
 def fa_fwd_tile(D, B=0, H=0, S=0):
@@ -268,4 +276,40 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                   cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, int(max_seqlen_q),
                   int(max_seqlen_k), total_q, total_k, D, causal, float(scale),
                   stream.cuda_stream, _dtype_code(q), strides)
+    return out, lse
+
+
+def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, causal: bool,
+                  scale: float | None = None, out=None, lse=None, stream=None):
+    """Attention forward on 8-bit float inputs with per-tensor descales.
+
+    q, k, v: contiguous [B, H, S, D] device tensors of E4M3 codes
+    (torch.float8_e4m3fn, or uint8 holding the codes), D = 128; the value of
+    a code is its E4M3 value times the tensor's descale. Returns (o, lse):
+    o [B, H, S, D] bfloat16, lse [B, H, S] float32, enqueued on `stream`
+    (default: torch's current stream) without synchronising.
+    """
+    import torch
+    _check_inputs(q, k, v, 4)
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"8-bit inputs must be float8_e4m3fn or uint8 codes, not {q.dtype}")
+    if q.shape != k.shape:
+        raise ValueError("q, k, v must have one shape [B, H, S, D]")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("8-bit inputs must be contiguous [B, H, S, D]")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if (out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous()
+            or lse.dtype != torch.float32 or lse.shape != (B, H, S) or not lse.is_contiguous()):
+        raise ValueError("out must be contiguous bf16 [B, H, S, D], lse contiguous fp32 [B, H, S]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+               B, H, S, D, causal, float(scale), float(descale_q), float(descale_k),
+               float(descale_v), stream.cuda_stream)
     return out, lse

@@ -17,7 +17,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_fwd_fp8.hip")]
 OUT = os.path.join(HERE, "libfa_fwd.so")
 ARCH = "gfx950"
 
@@ -42,7 +42,7 @@ def compile_flags() -> list[str]:
 
 def build(verbose: bool = False, save_temps: str | None = None, resource_usage: bool = False) -> str:
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *compile_flags(), SRC, "-o", tmp]
+    cmd = [hipcc(), *compile_flags(), *SRCS, "-o", tmp]
     if resource_usage:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     if save_temps:
@@ -52,8 +52,7 @@ def build(verbose: bool = False, save_temps: str | None = None, resource_usage: 
         print(" ".join(cmd), flush=True)
     cwd = save_temps or None
     if save_temps:
-        cmd[-3] = SRC
-        cmd[-1] = os.path.abspath(tmp) if not cmd[-1].startswith("-") else cmd[-1]
+        cmd[cmd.index("-o") + 1] = os.path.abspath(tmp)
     r = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
     out = (r.stdout or "") + (r.stderr or "")
     # the host pass does not know the device-only target feature

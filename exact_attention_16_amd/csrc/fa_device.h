@@ -1,0 +1,181 @@
+// Device building blocks shared by the gfx950 attention-forward kernels:
+// vector types, lane exchanges, buffer descriptors, LDS pointer types,
+// barriers and waits, scheduling patterns, and the Problem a launch solves.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_layout.h"
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+// Word 3 of a raw (untyped, stride 0) gfx9 buffer descriptor.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <int N> struct IC { static constexpr int value = N; };
+template <int P, class X> __device__ __forceinline__ X& pick(X& one, X& zero) {
+  if constexpr (P != 0) return one; else return zero;
+}
+
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Value combined with the same register of lane l^32 (the other k-half of
+// the same query row): v_permlane32_swap exchanges the upper half-wave of
+// one copy with the lower half-wave of the other, so the two results hold
+// both values in every lane and a symmetric op combines them.
+// The maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950):
+// fmaxf's NaN-ignoring form costs an extra quieting op per operand that
+// does not come from plain arithmetic (MFMA results, lane exchanges). A NaN
+// score makes its row NaN through the exponential either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return vmax(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Raw buffer descriptor over `bytes` bytes at `base`. A macro rather than a
+// function: a function or lambda returning the descriptor type makes the
+// host compilation pass drop the kernel launch stubs.
+#define FA_RSRC(base, bytes) \
+  __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>((const void*)(base)), 0, (int)(bytes), kBufferWord3)
+
+// LDS pointers stay in address space 3 from the point where each shared
+// array is declared (a cast of a generic pointer to address space 3 would
+// make the host compilation pass drop the kernel launch stubs).
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ u32x4 lds16(const lds_char* p) { return *(lds_u32x4*)p; }
+
+// Hardware work-group barrier fenced against compiler reordering. Unlike
+// __syncthreads() it implies no wait for outstanding memory operations: the
+// caller waits for exactly what it needs first.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0) (no export wait), 0 <= N <= 15.
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N <= 15, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);
+}
+
+// Scheduling pattern for one region: DS0 LDS reads up front, then REPS
+// times {one MFMA, V1 VALU, DS LDS reads, one MFMA, V2 VALU}.
+template <int DS0, int REPS, int V1, int DS, int V2>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+  for (int i = 0; i < REPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V2, 0);
+  }
+}
+
+// Scheduling pattern for one MFMA loop: DS0 LDS reads up front, then N
+// times {one MFMA, DS LDS reads}, so that each MFMA's operands are read
+// several MFMAs ahead of it. (Left to itself the scheduler reads them just
+// before their MFMA, which then waits for the LDS round trip.)
+template <int DS0, int N, int DS>
+__device__ __forceinline__ void read_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+  }
+}
+
+// What one launch computes, passed to the kernels by value. Strides are in
+// elements; a row is D contiguous elements. Without per-sequence offsets
+// (cuq == nullptr) sequence b, head h has Sq query rows starting at
+// q + b*qb + h*qh (row stride qs) and Sk key rows in k and v likewise; o has
+// q's row count and lse is Sq floats at lse + b*lb + h*lh. With offsets,
+// sequence b's query rows are token rows cuq[b] .. cuq[b+1]-1 (so its rows
+// start at q + cuq[b]*qs + h*qh, lse + h*lh + cuq[b]) and its key rows are
+// token rows cuk[b] .. cuk[b+1]-1; the kernel clamps both ranges to the
+// totq / totk token rows the tensors hold and the lengths to Sq / Sk.
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os, lb, lh;
+  const int* cuq;
+  const int* cuk;
+  int totq, totk;
+  int B, H, Sq, Sk;
+  int nqt;  // query tiles per (sequence, head) for the kernel's block of rows
+  float c;  // scale * log2(e) (8-bit inputs: times the Q and K descales)
+  unsigned long long* events;
+  float vscale;  // 8-bit inputs: the V descale, applied to O at the end
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Lengths and row-0 element offsets of sequence bb, head h of a Problem:
+// query rows Lq and key rows Lk (with per-sequence offsets: clamped to the
+// tensors' token rows and to Sq / Sk), and where row 0 of q, k, v, o and lse
+// starts.
+struct HeadRows {
+  int Lq, Lk;
+  long long q0, k0, v0, o0, l0;
+};
+__device__ __forceinline__ HeadRows head_rows(const Problem& P, int bb, int h) {
+  HeadRows r;
+  if (P.cuq) {
+    const int sq = clampi(P.cuq[bb], 0, P.totq), eq = clampi(P.cuq[bb + 1], sq, P.totq);
+    const int sk = clampi(P.cuk[bb], 0, P.totk), ek = clampi(P.cuk[bb + 1], sk, P.totk);
+    r.Lq = min(eq - sq, P.Sq);
+    r.Lk = min(ek - sk, P.Sk);
+    r.q0 = sq * P.qs + h * P.qh;
+    r.k0 = sk * P.ks + h * P.kh;
+    r.v0 = sk * P.vs + h * P.vh;
+    r.o0 = sq * P.os + h * P.oh;
+    r.l0 = h * P.lh + sq;
+  } else {
+    r.Lq = P.Sq;
+    r.Lk = P.Sk;
+    r.q0 = bb * P.qb + h * P.qh;
+    r.k0 = bb * P.kb + h * P.kh;
+    r.v0 = bb * P.vb + h * P.vh;
+    r.o0 = bb * P.ob + h * P.oh;
+    r.l0 = bb * P.lb + h * P.lh;
+  }
+  return r;
+}
+
+template <int R, class X> __device__ __forceinline__ X pick3(X a, X b, X c) {
+  if constexpr (R == 0) return a;
+  else if constexpr (R == 1) return b;
+  else return c;
+}
+
+}  // namespace fa

@@ -51,29 +51,11 @@
 #include <stdint.h>
 
 #include "../../include/fa_fwd.h"
-#include "fa_layout.h"
+#include "fa_device.h"
+#include "fa_layout8.h"
+#include "fa_pingpong.h"
 
 namespace fa {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLog2e = 1.442695040888963407f;
-// Word 3 of a raw (untyped, stride 0) gfx9 buffer descriptor.
-constexpr int kBufferWord3 = 0x00020000;
-
-template <int N> struct IC { static constexpr int value = N; };
-template <int P, class X> __device__ __forceinline__ X& pick(X& one, X& zero) {
-  if constexpr (P != 0) return one; else return zero;
-}
 
 template <typename T> struct Ops;
 
@@ -98,41 +80,6 @@ template <> struct Ops<_Float16> {
   }
 };
 
-// Value combined with the same register of lane l^32 (the other k-half of
-// the same query row): v_permlane32_swap exchanges the upper half-wave of
-// one copy with the lower half-wave of the other, so the two results hold
-// both values in every lane and a symmetric op combines them.
-// The maxima use the NaN-propagating maximum (v_maximum3_f32 on gfx950):
-// fmaxf's NaN-ignoring form costs an extra quieting op per operand that
-// does not come from plain arithmetic (MFMA results, lane exchanges). A NaN
-// score makes its row NaN through the exponential either way.
-__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float max_xor32(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return vmax(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
-}
-
-// Raw buffer descriptor over `bytes` bytes at `base`. A macro rather than a
-// function: a function or lambda returning the descriptor type makes the
-// host compilation pass drop the kernel launch stubs.
-#define FA_RSRC(base, bytes) \
-  __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>((const void*)(base)), 0, (int)(bytes), kBufferWord3)
-
-// LDS pointers stay in address space 3 from the point where each shared
-// array is declared (a cast of a generic pointer to address space 3 would
-// make the host compilation pass drop the kernel launch stubs).
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ u32x4 lds16(const lds_char* p) { return *(lds_u32x4*)p; }
-
 // V^T operand: two transposed 8-byte reads (keys +0..3 and +4..7)
 __device__ __forceinline__ u32x4 lds_tr_pair(const lds_char* p, uint32_t second) {
   const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
@@ -140,76 +87,6 @@ __device__ __forceinline__ u32x4 lds_tr_pair(const lds_char* p, uint32_t second)
   const u32x2 x = __builtin_bit_cast(u32x2, x0), y = __builtin_bit_cast(u32x2, x1);
   return (u32x4){x[0], x[1], y[0], y[1]};
 }
-
-// Hardware work-group barrier fenced against compiler reordering. Unlike
-// __syncthreads() it implies no wait for outstanding memory operations: the
-// caller waits for exactly what it needs first.
-__device__ __forceinline__ void wg_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-// s_waitcnt vmcnt(N) lgkmcnt(0) (no export wait), 0 <= N <= 15.
-template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N <= 15, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);
-}
-
-// Scheduling pattern for one region: DS0 LDS reads up front, then REPS
-// times {one MFMA, V1 VALU, DS LDS reads, one MFMA, V2 VALU}.
-template <int DS0, int REPS, int V1, int DS, int V2>
-__device__ __forceinline__ void interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
-#pragma unroll
-  for (int i = 0; i < REPS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, V1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, V2, 0);
-  }
-}
-
-// Scheduling pattern for one MFMA loop: DS0 LDS reads up front, then N
-// times {one MFMA, DS LDS reads}, so that each MFMA's operands are read
-// several MFMAs ahead of it. (Left to itself the scheduler reads them just
-// before their MFMA, which then waits for the LDS round trip.)
-template <int DS0, int N, int DS>
-__device__ __forceinline__ void read_ahead() {
-  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
-  }
-}
-
-// What one launch computes, passed to the kernels by value. Strides are in
-// elements; a row is D contiguous elements. Without per-sequence offsets
-// (cuq == nullptr) sequence b, head h has Sq query rows starting at
-// q + b*qb + h*qh (row stride qs) and Sk key rows in k and v likewise; o has
-// q's row count and lse is Sq floats at lse + b*lb + h*lh. With offsets,
-// sequence b's query rows are token rows cuq[b] .. cuq[b+1]-1 (so its rows
-// start at q + cuq[b]*qs + h*qh, lse + h*lh + cuq[b]) and its key rows are
-// token rows cuk[b] .. cuk[b+1]-1; the kernel clamps both ranges to the
-// totq / totk token rows the tensors hold and the lengths to Sq / Sk.
-struct Problem {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
-  long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os, lb, lh;
-  const int* cuq;
-  const int* cuk;
-  int totq, totk;
-  int B, H, Sq, Sk;
-  int nqt;  // query tiles per (sequence, head) for the kernel's block of rows
-  float c;  // scale * log2(e)
-  unsigned long long* events;
-};
-
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // One wave's share of a work-group: its query rows, accumulators and the
 // per-tile operations on them.
@@ -223,6 +100,9 @@ struct Wave {
   static constexpr int NKC = BN / 16;  // P.V contraction steps (16 keys each)
   static constexpr int DPW = C::dmaPerWave;
   static constexpr uint32_t RB = C::rowBytes;
+  using Config = C;
+  using STile = f32x16[NKB];  // S^T of one KV tile
+  using PTile = u32x4[NKC];   // P of one KV tile as P.V operands
 
   int lane, wave, hh, q0w, qrow, qt;
   int Lq, Lk, off;  // this sequence's query and key rows; off = Lk - Lq (causal alignment)
@@ -252,26 +132,10 @@ struct Wave {
     int bh;
     block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh);
     const int bb = bh / P.H, h = bh - bb * P.H;
-    long long q0, k0, v0, o0, l0;  // element offsets of row 0
-    if (P.cuq) {
-      const int sq = clampi(P.cuq[bb], 0, P.totq), eq = clampi(P.cuq[bb + 1], sq, P.totq);
-      const int sk = clampi(P.cuk[bb], 0, P.totk), ek = clampi(P.cuk[bb + 1], sk, P.totk);
-      Lq = min(eq - sq, P.Sq);
-      Lk = min(ek - sk, P.Sk);
-      q0 = sq * P.qs + h * P.qh;
-      k0 = sk * P.ks + h * P.kh;
-      v0 = sk * P.vs + h * P.vh;
-      o0 = sq * P.os + h * P.oh;
-      l0 = h * P.lh + sq;
-    } else {
-      Lq = P.Sq;
-      Lk = P.Sk;
-      q0 = bb * P.qb + h * P.qh;
-      k0 = bb * P.kb + h * P.kh;
-      v0 = bb * P.vb + h * P.vh;
-      o0 = bb * P.ob + h * P.oh;
-      l0 = bb * P.lb + h * P.lh;
-    }
+    const HeadRows hr = head_rows(P, bb, h);
+    Lq = hr.Lq;
+    Lk = hr.Lk;
+    const long long q0 = hr.q0, k0 = hr.k0, v0 = hr.v0, o0 = hr.o0, l0 = hr.l0;
     if (qt * C::BM >= Lq) return false;
     off = Lk - Lq;
     Kh = (const char*)P.k + k0 * 2;
@@ -362,6 +226,10 @@ struct Wave {
         o[jd] = Ops<T>::mfma(lds_tr_pair(vt + (voff0 ^ (uint32_t)(jd << 6)) + kc * 16 * RB, 4 * RB),
                              p[kc], o[jd]);
   }
+  // scheduling patterns of the two products: operands read several MFMAs
+  // ahead (two reads per P.V MFMA and one per S MFMA, four MFMAs ahead)
+  static __device__ __forceinline__ void pv_schedule() { read_ahead<8, NKC * NDB, 2>(); }
+  static __device__ __forceinline__ void qk_schedule() { read_ahead<4, NDC * NKB, 1>(); }
   // the tile starting at key kv0 needs index compares (diagonal or ragged end)
   __device__ __forceinline__ bool needs_mask(int kv0) const {
     return (CAUSAL && kv0 + BN - 1 > q0w + off) || kv0 + BN > Lk;
@@ -460,137 +328,11 @@ struct Wave {
 };
 
 // ------------------------------------------------- eight-wave ping-pong
-template <int R, class X> __device__ __forceinline__ X pick3(X a, X b, X c) {
-  if constexpr (R == 0) return a;
-  else if constexpr (R == 1) return b;
-  else return c;
-}
-
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_pp(const Problem P) {
-  using C = Cfg8<D>;
-  using W = Wave<T, C, CAUSAL, THR, DIAG>;
-  constexpr int TB = C::tileBytes;
-  constexpr int DPW = C::dmaPerWave;
-  constexpr bool ONE = pp_one_barrier<D>;  // one barrier per step, else two
-  static_assert(kStages == 3, "the step below is unrolled over three stages");
-  // One array per stage: with the stage fixed at compile time the compiler
-  // sees that an LDS read never aliases the DMA in flight into another stage
-  // and inserts no wait for it. The compiler lays the arrays out in name
-  // order; the V stages are named to come first, so that their transposed
-  // reads (two per P.V MFMA, the part of the MFMA phase with the most
-  // instructions per MFMA) mostly fit the 16-bit offset field of the LDS
-  // instruction and need no address arithmetic. This affects speed only.
-  __shared__ __attribute__((aligned(1024))) char a_vstage0[TB];
-  __shared__ __attribute__((aligned(1024))) char a_vstage1[TB];
-  __shared__ __attribute__((aligned(1024))) char a_vstage2[TB];
-  __shared__ __attribute__((aligned(1024))) char b_kstage0[TB];
-  __shared__ __attribute__((aligned(1024))) char b_kstage1[TB];
-  __shared__ __attribute__((aligned(1024))) char b_kstage2[TB];
-  lds_char* const lk0 = (lds_char*)b_kstage0;
-  lds_char* const lk1 = (lds_char*)b_kstage1;
-  lds_char* const lk2 = (lds_char*)b_kstage2;
-  lds_char* const lv0 = (lds_char*)a_vstage0;
-  lds_char* const lv1 = (lds_char*)a_vstage1;
-  lds_char* const lv2 = (lds_char*)a_vstage2;
-
-  W w;
-  if (!w.init(P)) return;
-  const int grp = w.wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
-  const int ntiles = w.group_tiles();
-  const int nw = w.wave_tiles();
-  f32x16 s[W::NKB];  // S(j), from its MFMA phase to its softmax phase
-  u32x4 p[W::NKC];   // P(j), from its softmax phase to the next MFMA phase
-
-  // DMA pair i (issued in slot 2i, R = i mod 3): K(i+2) and V(i+1), as
-  // empty ranges where those tiles do not exist, so that every pair is the
-  // same 2*DPW issues and each wait below is a constant count.
-  auto dma_pair = [&](auto r, int i) {
-    constexpr int R = decltype(r)::value;
-    w.dma_k(pick3<(R + 2) % 3>(lk0, lk1, lk2), i + 2, ntiles);
-    w.dma_v(pick3<(R + 1) % 3>(lv0, lv1, lv2), i + 1, ntiles);
-  };
-  // End of a slot: this wave's LDS reads are done and all its DMA except the
-  // latest pair has landed; then the work-group barrier.
-  auto end_slot = [&]() {
-    wait_vm_lgkm0<2 * DPW>();
-    wg_barrier();
-  };
-
-  // prologue: K(0), K(1), V(0) in their stages; the other stages get empty
-  // ranges so that the compiler tracks a DMA into every stage from the first
-  // block on (an LDS read then waits only for DMA into its own stage).
-  w.dma_k(lk0, 0);
-  w.dma_k(lk1, 1, ntiles);
-  w.dma_k(lk2, 2, 0);
-  w.dma_v(lv0, 0);
-  w.dma_v(lv1, 1, 0);
-  w.dma_v(lv2, 2, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  wg_barrier();
-
-  // With two barriers per step group A runs step j in slots (2j, 2j+1),
-  // group B in (2j+1, 2j+2): B takes slot 0 alone first and A takes the last
-  // slot alone at the end, so both groups pass the same number of barriers.
-  // With one, slot j holds A's step j and B's softmax phase of step j-1 and
-  // MFMA phase of step j. Each group has its own
-  // copy of the loop, in which every DMA is unconditional: the compiler's
-  // count of DMA in flight then matches the constant waits on every path.
-  auto run = [&](auto g) {
-    constexpr int G = decltype(g)::value;
-    if constexpr (G == 1) {
-      dma_pair(IC<0>{}, 0);
-      if constexpr (!ONE) end_slot();
-    }
-    // step j (R = j mod 3): MFMA phase P(j-1).V(j-1) + S(j) = K(j) Q^T, then
-    // the softmax phase of S(j). K(j) sits in stage R, V(j-1) in stage R-1.
-    // The MFMA phase runs at raised wave priority, so that on each SIMD the
-    // multiplying wave's MFMAs and LDS reads issue ahead of the other
-    // wave's exponentials whenever both are ready.
-    auto step = [&](auto r, int j) {
-      constexpr int R = decltype(r)::value;
-      __builtin_amdgcn_s_setprio(1);
-      if constexpr (G == 0) dma_pair(r, j);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j >= 1 && j - 1 < nw) {
-        w.pv(p, pick3<(R + 2) % 3>(lv0, lv1, lv2));
-        read_ahead<8, W::NKC * W::NDB, 2>();  // two reads per MFMA, four MFMAs ahead
-      }
-      if (j < nw) {
-        w.qk(s, pick3<R>(lk0, lk1, lk2));
-        read_ahead<4, W::NDC * W::NKB, 1>();  // one read per MFMA, four MFMAs ahead
-      }
-      if constexpr (ONE) {
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (G == 1) end_slot();
-      } else {
-        end_slot();
-      }
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j < nw) w.softmax_tile(s, p, j);
-      // group B's DMA share goes after its softmax work, clear of group A's
-      // issues at the start of the slot
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (G == 1) dma_pair(IC<(R + 1) % 3>{}, j + 1);
-      if constexpr (!ONE || G == 0) end_slot();
-    };
-    for (int j = 0;; j += 3) {
-      step(IC<0>{}, j);
-      if (j + 1 > ntiles) break;
-      step(IC<1>{}, j + 1);
-      if (j + 2 > ntiles) break;
-      step(IC<2>{}, j + 2);
-      if (j + 3 > ntiles) break;
-    }
-    if constexpr (G == 0 && !ONE) end_slot();
-  };
-  if (grp == 0) run(IC<0>{});
-  else run(IC<1>{});
-  __builtin_amdgcn_s_waitcnt(0);  // no DMA into LDS outlives the work-group
-  w.epilogue(P.events);
+  pp_body<Wave<T, Cfg8<D>, CAUSAL, THR, DIAG>>(P);
 }
 
 // ------------------------------------------------- four waves x 64 rows
@@ -1034,6 +776,51 @@ static int make_fixed(Problem* P, const void* q, const void* k, const void* v, v
   return validate_problem(*P, D, nq, sq_, sk_, sv_, so_, nk, 3, nl, sl, 3);
 }
 
+// 8-bit inputs (fa_fwd_fp8.hip)
+int launch_fp8(Problem P, int causal, hipStream_t stream);
+
+static bool positive_finite(float x) { return x > 0.f && isfinite(x); }
+
+// Dense [B,H,S,D] problem on E4M3 inputs (one byte per element) with a bf16
+// output (two bytes per element).
+static int make_fp8(Problem* P, const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int S, int D, int causal, float scale, float dq, float dk,
+                    float dv, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || S < 0) return FA_ERR_DIM;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (D != 128) return FA_ERR_UNSUPPORTED;
+  if (!positive_finite(scale) || !positive_finite(dq) || !positive_finite(dk) ||
+      !positive_finite(dv))
+    return FA_ERR_SCALE;
+  // the folded base-2 logit multiplier must be a normal float
+  const double c = (double)scale * dq * dk * (double)kLog2e;
+  if (!(c >= 1.17549435e-38 && c <= 3.40282347e38)) return FA_ERR_SCALE;
+  if ((long long)B * H * num_q_tiles(S, CfgF8::BM) >= (1LL << 31)) return FA_ERR_DIM;
+  if ((long long)B * H * S == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15)
+    return FA_ERR_ALIGN;
+  // one head's O rows addressed with 32-bit byte offsets; at most 2^40 elements
+  if ((long long)S * D * 2 >= (1LL << 31)) return FA_ERR_DIM;
+  const long long n = (long long)B * H * S * D;
+  if (n > (1LL << 40)) return FA_ERR_DIM;
+  const Span sq{(uintptr_t)q, (uintptr_t)q + (uintptr_t)n}, sk{(uintptr_t)k, (uintptr_t)k + (uintptr_t)n},
+      sv{(uintptr_t)v, (uintptr_t)v + (uintptr_t)n}, so{(uintptr_t)o, (uintptr_t)o + (uintptr_t)(2 * n)},
+      sl{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(4LL * B * H * S)};
+  if (spans_overlap(so, sq) || spans_overlap(so, sk) || spans_overlap(so, sv) ||
+      spans_overlap(sl, sq) || spans_overlap(sl, sk) || spans_overlap(sl, sv) ||
+      spans_overlap(sl, so))
+    return FA_ERR_ALIAS;
+  const long long hs = (long long)S * D;
+  *P = Problem{q, k, v, o, lse, H * hs, hs, D, H * hs, hs, D, H * hs, hs, D, H * hs, hs, D,
+               (long long)H * S, S, nullptr, nullptr, 0, 0, B, H, S, S, 0, (float)c, nullptr, dv};
+  return FA_OK;
+}
+
 static void dense_strides(long long* st, int H, int S, int D) {
   const long long hs = (long long)S * D;
   const long long v[] = {H * hs, hs, D, H * hs, hs, D, H * hs, hs, D, H * hs, hs, D,
@@ -1155,6 +942,17 @@ const char* fa_strerror(int status) {
   }
 }
 
-int fa_version(void) { return 300; }
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int S, int D, int causal, float scale, float descale_q, float descale_k,
+               float descale_v, hipStream_t stream) {
+  fa::Problem P;
+  bool empty;
+  const int r = fa::make_fp8(&P, q, k, v, o, lse, B, H, S, D, causal, scale, descale_q,
+                             descale_k, descale_v, &empty);
+  if (r != FA_OK || empty) return r;
+  return fa::launch_fp8(P, causal, stream);
+}
+
+int fa_version(void) { return 310; }
 
 }  // extern "C"

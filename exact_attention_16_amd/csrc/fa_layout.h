@@ -27,18 +27,19 @@ constexpr int kRowsPerWave = 32;  // query rows owned by one wave (one MFMA colu
 
 // A kernel configuration: head dimension D, NW waves (64 lanes) per
 // work-group, BN keys per KV tile, RPW query rows per wave (one or two
-// 32-row MFMA column blocks). One K or V tile in LDS holds BN rows (keys) of
-// D 16-bit elements, row-major, each row split in 16-byte chunks whose order
-// is XOR-swizzled per row.
-template <int D_, int NW_, int BN_, int RPW_ = kRowsPerWave> struct Cfg {
+// 32-row MFMA column blocks), ES bytes per K/V element. One K or V tile in
+// LDS holds BN rows (keys) of D elements, row-major, each row split in
+// 16-byte chunks whose order is XOR-swizzled per row.
+template <int D_, int NW_, int BN_, int RPW_ = kRowsPerWave, int ES_ = 2> struct Cfg {
   static constexpr int D = D_;
   static constexpr int NW = NW_;
   static constexpr int BN = BN_;
   static constexpr int RPW = RPW_;
+  static constexpr int ES = ES_;                         // bytes per K/V element
   static constexpr int threads = 64 * NW;
   static constexpr int BM = RPW * NW;                    // query rows per work-group
-  static constexpr int rowBytes = D * 2;
-  static constexpr int chunks = D / 8;                   // 16-byte chunks per row
+  static constexpr int rowBytes = D * ES;
+  static constexpr int chunks = rowBytes / 16;           // 16-byte chunks per row
   static constexpr int tileBytes = BN * rowBytes;        // one K or V tile
   static constexpr int dmaPerWave = tileBytes / 1024 / NW;  // 1-KiB DMA issues per wave
   static constexpr int rowsPerBlock = 64 / chunks;       // rows filled by one DMA issue

@@ -202,6 +202,40 @@ int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse
 int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n,
                 int* threads, long long* work_groups);
 
+/*
+ * fa_fwd_fp8 -- fa_fwd on 8-bit float inputs with one descale per tensor:
+ * the FP8 support that "FlashAttention的Triton性能考古学" (hotdry.top,
+ * section "架构感知优化策略") lists for newer GPUs.
+ *
+ *   q, k, v  device, [B,H,S,D] E4M3 codes (OCP 8-bit float: 1 sign, 4
+ *            exponent bits with bias 7, 3 mantissa bits; no infinities,
+ *            S.1111.111 is NaN), one byte per element, 16-byte aligned
+ *   o        device, [B,H,S,D] bf16, 16-byte aligned, written
+ *   lse      device, [B,H,S] float, 16-byte aligned, written
+ *   descale_q, descale_k, descale_v
+ *            the value of a code x of q is decode(x) * descale_q, and
+ *            likewise for k and v; finite and > 0. The output is attention
+ *            of those values: o and lse as fa_fwd defines them with
+ *            x_ij = scale * descale_q * descale_k * <q_i, k_j>.
+ *   D        128 only (FA_ERR_UNSUPPORTED otherwise)
+ *   other arguments as for fa_fwd; any S >= 1; B*H*S == 0 is a no-op.
+ *
+ * Precision: the logits and the row sums are exact products accumulated in
+ * fp32, as in fa_fwd; the probabilities are rounded to E4M3 (after scaling
+ * by a power of two that keeps them in (0, 256]) before the P V product, so
+ * O carries up to 2^-4 relative error per probability, the rounding of the
+ * 8-bit matrix units; lse is not affected.
+ *
+ * Errors: a descale or scale not finite and > 0, or a product
+ * scale * descale_q * descale_k * log2(e) outside the normal float range:
+ * FA_ERR_SCALE; o or lse sharing bytes with q, k, v or each other:
+ * FA_ERR_ALIAS; S*D*2 >= 2^31 or B*H*S*D > 2^40: FA_ERR_DIM; the rest as
+ * for fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int S, int D, int causal, float scale,
+               float descale_q, float descale_k, float descale_v, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -24,7 +24,11 @@
 //    the kernel code runs them, every read of a stage finds the tile it
 //    expects, landed and published by a barrier, and no DMA overwrites a
 //    stage that a wave of either group still has to read.
-// All of it for both kernel configurations (four and eight waves).
+// All of it for every kernel configuration (four and eight waves, 16-bit),
+// and the same checks for the 8-bit kernel's layouts (fa_layout8.h): its
+// K operand reads, its transposed V reads through ds_read_b64_tr_b8 (within
+// 16 lanes: result lane i, byte e = byte i%8 of source lane 2e + i/8), the
+// accumulator-to-P key order, and its global Q loads and O stores.
 //
 // Prints a summary and "OK"; exits non-zero on any error.
 #include <algorithm>
@@ -34,7 +38,7 @@
 #include <set>
 #include <vector>
 
-#include "../../exact_attention_16_amd/csrc/fa_layout.h"
+#include "../../exact_attention_16_amd/csrc/fa_layout8.h"
 
 using namespace fa;
 
@@ -325,6 +329,198 @@ template <class C> static void check_lengths() {
       }
 }
 
+// ------------------------------------------------ 8-bit kernel (fa_layout8.h)
+static std::vector<long> dma_tile8(bool is_k, int* worst64) {
+  using C = CfgF8;
+  std::vector<long> tag(C::tileBytes, -1);  // one tag per byte (element)
+  *worst64 = 1;
+  for (int w = 0; w < C::NW; ++w)
+    for (int i = 0; i < C::dmaPerWave; ++i) {
+      std::vector<uint32_t> addr(64);
+      for (int p = 0; p < 64; ++p) {
+        const uint32_t dst = (is_k ? dma_lds_k<C>(w, i) : dma_lds_v<C>(w, i)) + 16 * p;
+        const uint32_t src = is_k ? dma_src_k8(w, i, p) : dma_src_v8(w, i, p);
+        for (uint32_t rs = C::rowBytes; rs <= C::rowBytes + 64; rs += 16)
+          CHECK((is_k ? dma_src_k8(w, i, p, rs) : dma_src_v8(w, i, p, rs)) ==
+                    (is_k ? dma_src_k8(w, 0, p, rs) + i * (uint32_t)C::dmaRowsK * rs
+                          : dma_src_v8(w, 0, p, rs) + i * (uint32_t)C::dmaRowsV * rs),
+                "8-bit DMA source stride w=%d i=%d p=%d rs=%u", w, i, p, rs);
+        addr[p] = dst;
+        CHECK(dst % 16 == 0 && dst + 16 <= (uint32_t)C::tileBytes, "DMA dst %u", dst);
+        CHECK(src % 16 == 0 && src + 16 <= (uint32_t)C::tileBytes, "DMA src %u", src);
+        const int row = src / C::rowBytes, d0 = src % C::rowBytes;
+        const uint32_t expect = is_k ? k8_off(row, d0 / 16) : v8_off(row, d0 / 16);
+        CHECK(expect == dst, "8-bit DMA slot mismatch w=%d i=%d p=%d", w, i, p);
+        for (int e = 0; e < 16; ++e) {
+          CHECK(tag[dst + e] == -1, "LDS byte %u written twice", dst + e);
+          tag[dst + e] = tag_of(row, d0 + e, C::D);
+        }
+      }
+      *worst64 = std::max(*worst64, conflict_degree(addr, 16, 64));
+    }
+  for (size_t e = 0; e < tag.size(); ++e) CHECK(tag[e] != -1, "LDS byte %zu never written", e);
+  return tag;
+}
+
+static void check_lds8() {
+  using C = CfgF8;
+  constexpr int D = C::D;
+  int kw, vw;
+  const std::vector<long> ktag = dma_tile8(true, &kw);
+  const std::vector<long> vtag = dma_tile8(false, &vw);
+
+  // ---- S^T operand reads: block kb, step j, half x
+  int kr[2] = {1, 1};
+  for (int kb = 0; kb < C::BN / 32; ++kb)
+    for (int j = 0; j < D / 64; ++j)
+      for (int x = 0; x < 2; ++x) {
+        std::vector<uint32_t> addr(64);
+        for (int lane = 0; lane < 64; ++lane) {
+          const uint32_t off = k8_read_off(kb, j, x, lane);
+          CHECK(off == (k8_read_off(0, 0, 0, lane) ^ (uint32_t)(j << 6 | x << 4)) +
+                           k8_block_rows(kb) * (uint32_t)C::rowBytes,
+                "k8_read_off is not step 0 XOR (j << 6 | x << 4) plus the block's rows");
+          addr[lane] = off;
+          CHECK(off % 16 == 0 && off + 16 <= (uint32_t)C::tileBytes, "K8 read off %u", off);
+          const int key = k8_key(kb, lane & 31);
+          for (int e = 0; e < 16; ++e)
+            CHECK(ktag[off + e] == tag_of(key, 64 * j + 32 * (lane >> 5) + 16 * x + e, D),
+                  "K8 read kb=%d j=%d x=%d lane=%d e=%d", kb, j, x, lane, e);
+        }
+        kr[0] = std::max(kr[0], conflict_degree(addr, 16, 64));
+        kr[1] = std::max(kr[1], conflict_degree(addr, 16, 32));
+      }
+
+  // ---- V^T operand: four transposed 8-byte reads per (jd, chunk)
+  int vr[2] = {1, 1};
+  for (int jd = 0; jd < D / 32; ++jd)
+    for (int c = 0; c < C::BN / 64; ++c)
+      for (int t = 0; t < 4; ++t) {
+        std::vector<uint32_t> addr(64);
+        long src[64][8];
+        for (int lane = 0; lane < 64; ++lane) {
+          const uint32_t off = v8_tr_off(jd, c, t, lane);
+          CHECK(off == (v8_tr_off(0, 0, 0, lane) ^ (uint32_t)(jd << 5)) +
+                           (uint32_t)((64 * c + 8 * t) * C::rowBytes),
+                "v8_tr_off is not block 0 XOR (jd << 5) plus 64c + 8t rows");
+          addr[lane] = off;
+          CHECK(off % 8 == 0 && off + 8 <= (uint32_t)C::tileBytes, "V8 read off %u", off);
+          for (int b = 0; b < 8; ++b) src[lane][b] = vtag[off + b];
+        }
+        for (int lane = 0; lane < 64; ++lane) {
+          const int g0 = lane & ~15, i = lane & 15;
+          const int d = 32 * jd + (lane & 31);
+          for (int e = 0; e < 8; ++e) {
+            const long got = src[g0 + 2 * e + i / 8][i % 8];
+            const int key = 64 * c + 32 * (lane >> 5) + 8 * t + e;
+            CHECK(got == tag_of(key, d, D), "V8^T read jd=%d c=%d t=%d lane=%d e=%d", jd, c, t,
+                  lane, e);
+          }
+        }
+        vr[0] = std::max(vr[0], conflict_degree(addr, 8, 64));
+        vr[1] = std::max(vr[1], conflict_degree(addr, 8, 32));
+      }
+
+  // ---- accumulator -> P operand key order
+  for (int kb = 0; kb < C::BN / 32; ++kb)
+    for (int hh = 0; hh < 2; ++hh)
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r / 4) + 4 * hh + (r % 4);  // MFMA row of element r
+        CHECK(k8_key(kb, row) == acc_key8(kb, r, hh), "8-bit acc key kb=%d r=%d hh=%d", kb, r, hh);
+      }
+  for (int c = 0; c < C::BN / 64; ++c)
+    for (int hh = 0; hh < 2; ++hh)
+      for (int e = 0; e < 32; ++e)  // byte e of the lane's P operand of chunk c
+        CHECK(acc_key8(2 * c + e / 16, e % 16, hh) == 64 * c + 32 * hh + e, "8-bit P key order");
+  std::set<int> keys;
+  for (int kb = 0; kb < C::BN / 32; ++kb)
+    for (int r = 0; r < 32; ++r) keys.insert(k8_key(kb, r));
+  CHECK((int)keys.size() == C::BN && *keys.begin() == 0 && *keys.rbegin() == C::BN - 1,
+        "8-bit K rows are not a permutation of the tile");
+
+  std::printf("8-bit D=%d waves=%d BN=%d tile=%d B: conflict degree (64 banks / 32 banks): K "
+              "operand read %d/%d, V^T transposed read %d/%d; DMA writes %d/%d (64 banks)\n",
+              D, C::NW, C::BN, C::tileBytes, kr[0], kr[1], vr[0], vr[1], kw, vw);
+  CHECK(kr[0] == 1 && kr[1] == 1, "8-bit K operand reads conflict");
+  CHECK(vr[0] == 1, "8-bit V^T reads conflict (64 banks)");
+  CHECK(kw == 1 && vw == 1, "8-bit DMA writes conflict");
+}
+
+// Global accesses of the 8-bit kernel for B*H heads of Sq x Sk: rows rs
+// bytes apart in q, k, v and rso bytes apart in o (16-bit output).
+static void check_global8(int B, int H, int Sq, int Sk, bool causal, uint32_t rs = 128,
+                          uint32_t rso = 256) {
+  using C = CfgF8;
+  const int BH = B * H, nqt = num_q_tiles(Sq, C::BM), BN = C::BN;
+  const long grid = (long)nqt * BH;
+  const uint32_t q_bytes = (uint32_t)Sq * rs, o_bytes = (uint32_t)Sq * rso;
+  const size_t head_elems = (size_t)Sq * C::D;
+  const bool track = head_elems * (size_t)BH <= ((size_t)1 << 26);
+  std::vector<char> seen(grid, 0), owritten(track ? head_elems * BH : 0, 0);
+  for (long bid = 0; bid < grid; ++bid) {
+    int qt, bh;
+    block_to_tile((int)bid, BH, nqt, causal, &qt, &bh);
+    const long cell = (long)qt * BH + bh;
+    CHECK(qt >= 0 && qt < nqt && bh >= 0 && bh < BH && !seen[cell], "8-bit tile map bid=%ld", bid);
+    seen[cell] = 1;
+    if (qt * C::BM >= Sq) continue;
+    const int ntiles = (tile_kv_end(qt, Sq, Sk, causal, C::BM) + BN - 1) / BN;
+    for (int t = 0; t < ntiles; ++t) {
+      const uint32_t range = (uint32_t)(Sk - t * BN) * rs;
+      for (int w = 0; w < C::NW; ++w)
+        for (int i = 0; i < C::dmaPerWave; ++i)
+          for (int p = 0; p < 64; ++p)
+            for (int kv = 0; kv < 2; ++kv) {
+              const uint32_t o = kv ? dma_src_v8(w, i, p, rs) : dma_src_k8(w, i, p, rs);
+              const int row = o / rs;
+              CHECK(o % rs + 16 <= (uint32_t)C::rowBytes, "8-bit DMA chunk leaves its row");
+              if (t * BN + row < Sk)
+                CHECK(o + 16 <= range, "8-bit DMA in-range row crosses the end");
+              else
+                CHECK(o >= range, "8-bit DMA row past Sk not wholly out of range");
+            }
+    }
+    for (int wave = 0; wave < C::NW; ++wave) {
+      const int q0w = qt * C::BM + wave * C::RPW;
+      const bool live = q0w < Sq;
+      const int nw = live ? (wave_kv_end(q0w, Sq, Sk, causal) + BN - 1) / BN : 0;
+      CHECK(nw <= ntiles, "8-bit wave computes a tile the work-group does not load");
+      for (int lane = 0; lane < 64; ++lane) {
+        const int qrow = q0w + (lane & 31), hh = lane >> 5;
+        for (int j = 0; j < C::D / 64; ++j)
+          for (int x = 0; x < 2; ++x) {
+            const uint32_t o = q8_frag_off(qrow, j, hh, x, rs);
+            if (qrow < Sq)
+              CHECK(o + 16 <= q_bytes && o % rs + 16 <= (uint32_t)C::rowBytes, "Q8 load out of bounds");
+            else
+              CHECK(o >= q_bytes, "Q8 row past Sq not wholly out of range");
+          }
+        if (!live) continue;
+        for (int jd = 0; jd < C::D / 32; ++jd)
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t o = o8_frag_off(qrow, jd, u, hh, rso);
+            if (qrow >= Sq) {
+              CHECK(o >= o_bytes, "O8 store past Sq not wholly out of range");
+              continue;
+            }
+            CHECK(o + 8 <= o_bytes && o % rso + 8 <= (uint32_t)C::D * 2, "O8 store out of bounds");
+            // accumulator elements 4u + e of d-block jd are d = 32jd + 8u + 4hh + e
+            CHECK((o % rso) / 2 == (uint32_t)(32 * jd + 8 * u + 4 * hh), "O8 column");
+            if (track)
+              for (int e = 0; e < 4; ++e) {
+                const size_t pe = (size_t)bh * head_elems + (size_t)(o / rso) * C::D + (o % rso) / 2 + e;
+                CHECK(!owritten[pe], "O8 element written twice");
+                owritten[pe] = 1;
+              }
+          }
+      }
+    }
+  }
+  for (long c = 0; c < grid; ++c) CHECK(seen[c], "8-bit tile never visited");
+  if (track)
+    for (size_t p = 0; p < owritten.size(); ++p) CHECK(owritten[p], "O8 element not written");
+}
+
 // ------------------------------------------------ ping-pong schedule replay
 // One DMA share (one wave's issues) of a tile into a stage.
 struct Share {
@@ -536,6 +732,19 @@ int main() {
   check_global<CfgW2<128>>(2, 16, 8192, true);
   check_global<CfgW2<64>>(10, 64, 1024, false);
   check_global<CfgW2<128>>(1, 1, 65536, true);
+  // 8-bit kernel
+  check_lds8();
+  for (auto& s : shapes)
+    for (int causal = 0; causal < 2; ++causal) check_global8(s[0], s[1], s[2], s[2], causal);
+  {
+    const int lens[] = {1, 31, 64, 127, 128, 129, 255, 256, 257, 513};
+    for (int lq : lens)
+      for (int lk : lens)
+        for (int causal = 0; causal < 2; ++causal)
+          check_global8(1, 2, lq, lk, causal != 0, 128 + 32, 256 + 64);
+  }
+  check_global8(2, 16, 8192, 8192, true);
+  std::printf("8-bit kernel: shapes, length pairs, full size: checked\n");
   if (g_err) {
     std::printf("FAILED with %d errors\n", g_err);
     return 1;

@@ -24,8 +24,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == {"fa_fwd", "fa_fwd_f16", "fa_fwd_bf16", "fa_fwd_diag",
-                           "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_tile", "fa_strerror",
-                           "fa_version"}
+                           "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_tile",
+                           "fa_strerror", "fa_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -48,13 +48,14 @@ def test_kernel_launch_stubs_are_defined():
         pytest.skip("no nm")
     out = subprocess.run([nm, "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
     stubs = [l for l in out.splitlines() if "device_stub" in l]
-    # 3 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic thresholds)
-    assert len(stubs) == 72
+    # 3 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic
+    # thresholds), and the 8-bit kernel x 2 masks
+    assert len(stubs) == 74
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 300
+    assert fa.fa_version() == 310
     for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG, LAYOUT):
         assert fa.fa_strerror(st) and fa.fa_strerror(st) != "unknown status"
     assert fa.fa_strerror(12345) == "unknown status"
@@ -238,3 +239,43 @@ def test_varlen_validation(args, expect):
                                   dict(total_q=0, cu_q=0, cu_k=0, q=0)])
 def test_varlen_empty_is_a_noop(args):
     assert _varlen_call(**args) == OK
+
+
+# ------------------------------------------------ 8-bit inputs
+GOOD8 = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, S=100, D=128, causal=1, scale=0.125,
+             dq=0.01, dk=0.02, dv=0.5, stream=None)
+
+
+def _call8(**kw):
+    a = dict(GOOD8, **kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"],
+                         a["D"], a["causal"], a["scale"], a["dq"], a["dk"], a["dv"], a["stream"],
+                         check=False)
+
+
+NBYTES = 2 * 3 * 100 * 128  # one 8-bit input tensor of GOOD8
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL),
+    (dict(B=-1), DIM), (dict(S=-1), DIM), (dict(S=1 << 23), DIM),
+    (dict(B=1 << 16, H=1 << 16, S=1 << 12), DIM),
+    (dict(D=64), UNSUP), (dict(D=256), UNSUP),
+    (dict(k=K + 8), ALIGN), (dict(lse=L + 4), ALIGN),
+    (dict(scale=0.0), SCALE), (dict(dq=0.0), SCALE), (dict(dk=-1.0), SCALE),
+    (dict(dv=float("nan")), SCALE), (dict(dv=float("inf")), SCALE),
+    (dict(scale=1e-30, dq=1e-10), SCALE),          # folded multiplier underflows
+    (dict(scale=1e30, dq=1e10, dk=1e10), SCALE),   # overflows
+    # q, k, v span one byte per element, o two, lse four per row
+    (dict(o=Q + NBYTES - 16), ALIAS), (dict(o=V - 2 * NBYTES + 16), ALIAS),
+    (dict(lse=O + 2 * NBYTES - 16), ALIAS), (dict(lse=K), ALIAS),
+    (dict(causal=2), ARG),
+])
+def test_fp8_validation_rejects(kw, expect):
+    assert _call8(**kw) == expect
+
+
+def test_fp8_empty_problem_is_a_noop():
+    assert _call8(S=0) == OK
+    assert _call8(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
+    assert _call8(H=0, D=64) == UNSUP  # the head dimension is checked first
