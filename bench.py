@@ -50,16 +50,20 @@ METRIC = "attention fwd TFLOPS (B·H·S²·D·4, causal halved) + % of bf16 MFMA
 PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA peak (published 2.5 PFLOP/s)
 PEAK_TFLOPS_FP8 = 5033.2  # MI355X dense fp8 MFMA peak (published 5.0 PFLOP/s)
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_layout.h", "fa_device.h", "fa_pingpong.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_long_hbm_traffic.json")
+CSRC = os.path.join(ROOT, "exact_attention_16_amd", "csrc")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_hbm_traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """Hash of every kernel source file (.hip and .h)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -67,7 +71,7 @@ def load_traffic(workload: str):
     """HBM bytes per launch from the committed counter profile, if it was
     taken on the current kernel source; otherwise None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -123,8 +127,8 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> dict:
         "bytes_per_launch": fkib * 1024.0 * ff + wkib * 1024.0 * wf,
         "note": "scale = 1 GiB / (counter KiB x 1024) of the calibration copies",
     }
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    os.makedirs(os.path.dirname(traffic_file(workload)), exist_ok=True)
+    with open(traffic_file(workload), "w") as f:
         json.dump(out, f, indent=1)
     return out
 
@@ -236,14 +240,7 @@ def main(argv=None) -> int:
 
     torch.cuda.synchronize()
     if args.calibrate_copy:
-        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)  # 1 GiB
-        dst = torch.empty_like(src)
-        with torch.cuda.stream(stream):
-            for _ in range(3):
-                dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        print("calibrate-copy: 3 x 1 GiB device copies done", file=sys.stderr, flush=True)
+        calibrate_copy(torch, dev, stream)
 
     for _ in range(args.warmup):
         step()
@@ -315,6 +312,18 @@ def main(argv=None) -> int:
     return 0
 
 
+def calibrate_copy(torch, dev, stream):
+    """Three plain 1 GiB device copies (the known size HBM counters are scaled by)."""
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    print("calibrate-copy: 3 x 1 GiB device copies done", file=sys.stderr, flush=True)
+
+
 def timed(step, stream, torch, steps: int, warmup: int):
     """W untimed steps, then K timed back-to-back on `stream` (HIP events on
     that stream); returns (ms per step, wall seconds, median single-launch ms)."""
@@ -356,6 +365,8 @@ def bench_fp8(args, torch, fa, w) -> int:
                       stream.cuda_stream)
 
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev, stream)
     ms, wall, med = timed(step, stream, torch, args.steps, args.warmup)
     assert bool(torch.isfinite(lse).all()), "non-finite output"
     tflops = w.flops / (ms * 1e-3) / 1e12
@@ -365,9 +376,9 @@ def bench_fp8(args, torch, fa, w) -> int:
           f"Median single launch:      {med:.4f} ms", file=sys.stderr, flush=True)
     groups = w.B * w.H * -(-w.S // 256)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS_FP8, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_TFLOPS_FP8, "traffic": None,
-                "kernel": f"fa_fwd_pp8<causal={int(w.causal)}> ({groups} work-groups x 512 "
-                          f"threads, 256 query rows, 128-key tiles)",
+                "frac": tflops / PEAK_TFLOPS_FP8, "traffic": load_traffic(w.name),
+                "kernel": f"fa_fwd_il8<causal={int(w.causal)}> ({groups} work-groups x 512 "
+                          f"threads, 256 query rows, 64-key tiles)",
                 "flops_per_launch": w.flops, "avg_launch_ms": ms, "median_launch_ms": med,
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes}
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, qc, kc, vc, descale=ds)

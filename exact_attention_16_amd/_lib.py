@@ -25,6 +25,7 @@ VARIANT_AUTO = 0
 VARIANT_FOUR_WAVE = 1
 VARIANT_PING_PONG = 2
 VARIANT_TWO_BLOCK = 3
+VARIANT_INTERLEAVE = 4
 
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_DIM", -3: "FA_ERR_UNSUPPORTED",

@@ -112,6 +112,19 @@ __device__ __forceinline__ void read_ahead() {
   }
 }
 
+// Scheduling pattern for one region of independent MFMA and vector work:
+// DS0 LDS reads up front, then N times {one MFMA, DS LDS reads, V VALU}.
+template <int DS0, int N, int DS, int V>
+__device__ __forceinline__ void mix() {
+  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
 // What one launch computes, passed to the kernels by value. Strides are in
 // elements; a row is D contiguous elements. Without per-sequence offsets
 // (cuq == nullptr) sequence b, head h has Sq query rows starting at

@@ -53,6 +53,7 @@
 #include "../../include/fa_fwd.h"
 #include "fa_device.h"
 #include "fa_layout8.h"
+#include "fa_interleave.h"
 #include "fa_pingpong.h"
 
 namespace fa {
@@ -230,6 +231,11 @@ struct Wave {
   // ahead (two reads per P.V MFMA and one per S MFMA, four MFMAs ahead)
   static __device__ __forceinline__ void pv_schedule() { read_ahead<8, NKC * NDB, 2>(); }
   static __device__ __forceinline__ void qk_schedule() { read_ahead<4, NDC * NKB, 1>(); }
+  // softmax of one tile (about 4.5 vector instructions per score, BN / 2
+  // scores per lane) spread over the next tile's S MFMAs
+  static __device__ __forceinline__ void il_schedule() {
+    mix<4, NDC * NKB, 1, (9 * BN / 4) / (NDC * NKB) + 1>();
+  }
   // the tile starting at key kv0 needs index compares (diagonal or ragged end)
   __device__ __forceinline__ bool needs_mask(int kv0) const {
     return (CAUSAL && kv0 + BN - 1 > q0w + off) || kv0 + BN > Lk;
@@ -333,6 +339,14 @@ __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_pp(const Problem P) {
   pp_body<Wave<T, Cfg8<D>, CAUSAL, THR, DIAG>>(P);
+}
+
+// ------------------------------------------------- eight waves, interleaved
+template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_il(const Problem P) {
+  il_body<Wave<T, CfgIL<D>, CAUSAL, THR, DIAG>>(P);
 }
 
 // ------------------------------------------------- four waves x 64 rows
@@ -626,7 +640,7 @@ fa_fwd_k4(const Problem P) {
 // one work-group per compute unit, else the four-wave kernel.
 constexpr long long kPingPongMinGroups = 256;
 
-enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kTwoBlock = 3 };
+enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kTwoBlock = 3, kInterleave = 4 };
 
 template <int D> static bool use_pingpong(int BH, int S, int variant) {
   if (variant == kFourWave) return false;
@@ -637,7 +651,11 @@ template <int D> static bool use_pingpong(int BH, int S, int variant) {
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 static int launch_one(Problem P, hipStream_t stream, int variant) {
   const int BH = P.B * P.H;
-  if (variant == kTwoBlock) {
+  if (variant == kInterleave) {
+    P.nqt = num_q_tiles(P.Sq, CfgIL<D>::BM);
+    hipLaunchKernelGGL((fa_fwd_il<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+                       dim3(CfgIL<D>::threads), 0, stream, P);
+  } else if (variant == kTwoBlock) {
     P.nqt = num_q_tiles(P.Sq, CfgW2<D>::BM);
     hipLaunchKernelGGL((fa_fwd_w2<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
                        dim3(CfgW2<D>::threads), 0, stream, P);
@@ -898,7 +916,7 @@ int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse
   const int r = fa::make_fixed(&P, q, k, v, o, lse, B, H, S, S, D, causal, scale, dtype, st, &empty);
   if (r != FA_OK) return r;
   if (threshold_log2 != 0 && threshold_log2 != 8) return FA_ERR_ARG;
-  if (variant < fa::kAuto || variant > fa::kTwoBlock) return FA_ERR_ARG;
+  if (variant < fa::kAuto || variant > fa::kInterleave) return FA_ERR_ARG;
   if (!rescale_events) return FA_ERR_NULL;
   if (((uintptr_t)rescale_events & 7) != 0) return FA_ERR_ALIGN;
   if (empty) return FA_OK;

@@ -2,10 +2,10 @@
 // tensor) for MI355X (gfx950): Q, K and V are E4M3 codes, O is bf16 and the
 // row logsumexp fp32.
 //
-// Same work-group as the 16-bit ping-pong kernel (fa_pingpong.h: eight
-// waves of 32 query rows, two groups alternating MFMA and softmax phases,
-// K/V in three LDS stages filled by direct DMA), with the 8-bit matrix
-// instruction v_mfma_f32_32x32x64_f8f6f4 for both products:
+// Work-group: eight waves of 32 query rows (fa_interleave.h), each
+// overlapping the softmax of KV tile j with the MFMAs of tile j+1's scores,
+// K/V in three LDS stages filled by direct DMA, 64-key tiles. Both products
+// use the 8-bit matrix instruction v_mfma_f32_32x32x64_f8f6f4:
 //   S^T = K Q^T   two 64-deep steps per 32-key block (D = 128)
 //   O^T += V^T P^T  one 64-key chunk per MFMA, P rounded to E4M3
 // The operand layouts (fa_layout8.h) put each lane's 32 S values of a 64-key
@@ -33,6 +33,7 @@
 #include "../../include/fa_fwd.h"
 #include "fa_device.h"
 #include "fa_layout8.h"
+#include "fa_interleave.h"
 #include "fa_pingpong.h"
 
 namespace fa {
@@ -61,11 +62,12 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// One wave's 32 query rows of the 8-bit kernel (the interface pp_body uses).
-template <bool CAUSAL, int THR>
+// One wave's 32 query rows of the 8-bit kernel (the interface il_body and
+// pp_body use).
+template <bool CAUSAL, int THR, class C_ = CfgF8>
 struct Wave8 {
-  using C = CfgF8;
-  using Config = CfgF8;
+  using C = C_;
+  using Config = C_;
   static constexpr int D = C::D;
   static constexpr int BN = C::BN;
   static constexpr int NKB = BN / 32;  // 32-key MFMA blocks of S per tile
@@ -129,8 +131,8 @@ struct Wave8 {
     }
     koff0 = k8_read_off(0, 0, 0, lane);
     voff0 = v8_tr_off(0, 0, 0, lane);
-    kdo0 = dma_src_k8(wave, 0, lane, rsk);
-    vdo0 = dma_src_v8(wave, 0, lane, rsv);
+    kdo0 = dma_src_k8<C>(wave, 0, lane, rsk);
+    vdo0 = dma_src_v8<C>(wave, 0, lane, rsv);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) o[j] = (f32x16){};
     b = -INFINITY;
@@ -198,6 +200,11 @@ struct Wave8 {
   // two reads per S MFMA, two MFMAs ahead
   static __device__ __forceinline__ void pv_schedule() { read_ahead<8, NCH * NDB, 4>(); }
   static __device__ __forceinline__ void qk_schedule() { read_ahead<4, NDJ * NKB, 2>(); }
+  // softmax of one tile (about 4 vector instructions per score, 2 BN / 64
+  // scores per lane) spread over the next tile's S MFMAs
+  static __device__ __forceinline__ void il_schedule() {
+    mix<4, NDJ * NKB, 2, (4 * BN / 2) / (NDJ * NKB)>();
+  }
 
   __device__ __forceinline__ bool needs_mask(int kv0) const {
     return (CAUSAL && kv0 + BN - 1 > q0w + off) || kv0 + BN > Lk;
@@ -289,18 +296,20 @@ struct Wave8 {
 template <bool CAUSAL>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa_fwd_pp8(const Problem P) {
-  pp_body<Wave8<CAUSAL, 2>>(P);
+fa_fwd_il8(const Problem P) {
+  il_body<Wave8<CAUSAL, 2, CfgF8i>>(P);
 }
 
-// Launches the 8-bit kernel for a filled, validated Problem.
+// Launches the 8-bit kernel for a filled, validated Problem. (The same wave
+// type also runs under the ping-pong body, pp_body<Wave8<CAUSAL, 2>> with
+// 128-key tiles; on the long causal workload that took 5% longer.)
 int launch_fp8(Problem P, int causal, hipStream_t stream) {
-  P.nqt = num_q_tiles(P.Sq, CfgF8::BM);
-  const dim3 grid((unsigned)P.nqt * (unsigned)(P.B * P.H)), block(CfgF8::threads);
+  P.nqt = num_q_tiles(P.Sq, CfgF8i::BM);
+  const dim3 grid((unsigned)P.nqt * (unsigned)(P.B * P.H)), block(CfgF8i::threads);
   if (causal)
-    hipLaunchKernelGGL(fa_fwd_pp8<true>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL(fa_fwd_il8<true>, grid, block, 0, stream, P);
   else
-    hipLaunchKernelGGL(fa_fwd_pp8<false>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL(fa_fwd_il8<false>, grid, block, 0, stream, P);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -61,6 +61,9 @@ template <int D> using Cfg8 = Cfg<D, 8, (D == 64 ? 128 : 96)>;
 // from LDS feeds both blocks' MFMAs, half the LDS traffic per FLOP of the
 // one-block kernels. 32-key tiles keep both blocks' S and P in registers.
 template <int D> using CfgW2 = Cfg<D, 4, 32, 64>;
+// Eight waves of 32 rows (256 rows), each interleaving its own softmax with
+// its next tile's MFMAs; 64-key tiles keep two S tiles in registers.
+template <int D> using CfgIL = Cfg<D, 8, 64>;
 
 // ------------------------------------------------------- work decomposition
 // One work-group per (Q tile, batch*head). Under a causal mask Q tile t needs

@@ -14,6 +14,8 @@ namespace fa {
 // 128 of one-byte elements: 128-byte rows, eight 16-byte chunks per row,
 // 16 KiB per K or V tile.
 using CfgF8 = Cfg<128, 8, 128, kRowsPerWave, 1>;
+// The interleaved 8-bit kernel: the same with 64-key tiles (one chunk).
+using CfgF8i = Cfg<128, 8, 64, kRowsPerWave, 1>;
 
 // ------------------------------------------------ MFMA lane mappings
 // v_mfma_f32_32x32x64_f8f6f4 (both operands E4M3): operand A row i / operand
@@ -57,14 +59,14 @@ FA_HD uint32_t v8_off(int r, int c) { return (uint32_t)(r * 128 + ((c ^ gv8(r)) 
 // (8 rows). K issues are NW blocks (64 rows) apart and gk8 reads row bits
 // 0, 1, 2 and 5 only; V issues are one block (8 rows) apart and gv8 reads row
 // bits 1, 2 only: issue i's source offset is issue 0's plus i rows strides.
-FA_HD uint32_t dma_src_k8(int w, int i, int lane, uint32_t rs = 128) {
+template <class C = CfgF8> FA_HD uint32_t dma_src_k8(int w, int i, int lane, uint32_t rs = 128) {
   int r, pc;
-  dma_slot<CfgF8>(dma_block_k<CfgF8>(w, i), lane, &r, &pc);
+  dma_slot<C>(dma_block_k<C>(w, i), lane, &r, &pc);
   return (uint32_t)r * rs + (uint32_t)((pc ^ gk8(r)) << 4);
 }
-FA_HD uint32_t dma_src_v8(int w, int i, int lane, uint32_t rs = 128) {
+template <class C = CfgF8> FA_HD uint32_t dma_src_v8(int w, int i, int lane, uint32_t rs = 128) {
   int r, pc;
-  dma_slot<CfgF8>(dma_block_v<CfgF8>(w, i), lane, &r, &pc);
+  dma_slot<C>(dma_block_v<C>(w, i), lane, &r, &pc);
   return (uint32_t)r * rs + (uint32_t)((pc ^ gv8(r)) << 4);
 }
 

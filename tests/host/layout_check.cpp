@@ -330,8 +330,7 @@ template <class C> static void check_lengths() {
 }
 
 // ------------------------------------------------ 8-bit kernel (fa_layout8.h)
-static std::vector<long> dma_tile8(bool is_k, int* worst64) {
-  using C = CfgF8;
+template <class C> static std::vector<long> dma_tile8(bool is_k, int* worst64) {
   std::vector<long> tag(C::tileBytes, -1);  // one tag per byte (element)
   *worst64 = 1;
   for (int w = 0; w < C::NW; ++w)
@@ -339,11 +338,11 @@ static std::vector<long> dma_tile8(bool is_k, int* worst64) {
       std::vector<uint32_t> addr(64);
       for (int p = 0; p < 64; ++p) {
         const uint32_t dst = (is_k ? dma_lds_k<C>(w, i) : dma_lds_v<C>(w, i)) + 16 * p;
-        const uint32_t src = is_k ? dma_src_k8(w, i, p) : dma_src_v8(w, i, p);
+        const uint32_t src = is_k ? dma_src_k8<C>(w, i, p) : dma_src_v8<C>(w, i, p);
         for (uint32_t rs = C::rowBytes; rs <= C::rowBytes + 64; rs += 16)
-          CHECK((is_k ? dma_src_k8(w, i, p, rs) : dma_src_v8(w, i, p, rs)) ==
-                    (is_k ? dma_src_k8(w, 0, p, rs) + i * (uint32_t)C::dmaRowsK * rs
-                          : dma_src_v8(w, 0, p, rs) + i * (uint32_t)C::dmaRowsV * rs),
+          CHECK((is_k ? dma_src_k8<C>(w, i, p, rs) : dma_src_v8<C>(w, i, p, rs)) ==
+                    (is_k ? dma_src_k8<C>(w, 0, p, rs) + i * (uint32_t)C::dmaRowsK * rs
+                          : dma_src_v8<C>(w, 0, p, rs) + i * (uint32_t)C::dmaRowsV * rs),
                 "8-bit DMA source stride w=%d i=%d p=%d rs=%u", w, i, p, rs);
         addr[p] = dst;
         CHECK(dst % 16 == 0 && dst + 16 <= (uint32_t)C::tileBytes, "DMA dst %u", dst);
@@ -362,12 +361,11 @@ static std::vector<long> dma_tile8(bool is_k, int* worst64) {
   return tag;
 }
 
-static void check_lds8() {
-  using C = CfgF8;
+template <class C> static void check_lds8() {
   constexpr int D = C::D;
   int kw, vw;
-  const std::vector<long> ktag = dma_tile8(true, &kw);
-  const std::vector<long> vtag = dma_tile8(false, &vw);
+  const std::vector<long> ktag = dma_tile8<C>(true, &kw);
+  const std::vector<long> vtag = dma_tile8<C>(false, &vw);
 
   // ---- S^T operand reads: block kb, step j, half x
   int kr[2] = {1, 1};
@@ -448,9 +446,9 @@ static void check_lds8() {
 
 // Global accesses of the 8-bit kernel for B*H heads of Sq x Sk: rows rs
 // bytes apart in q, k, v and rso bytes apart in o (16-bit output).
+template <class C>
 static void check_global8(int B, int H, int Sq, int Sk, bool causal, uint32_t rs = 128,
                           uint32_t rso = 256) {
-  using C = CfgF8;
   const int BH = B * H, nqt = num_q_tiles(Sq, C::BM), BN = C::BN;
   const long grid = (long)nqt * BH;
   const uint32_t q_bytes = (uint32_t)Sq * rs, o_bytes = (uint32_t)Sq * rso;
@@ -471,7 +469,7 @@ static void check_global8(int B, int H, int Sq, int Sk, bool causal, uint32_t rs
         for (int i = 0; i < C::dmaPerWave; ++i)
           for (int p = 0; p < 64; ++p)
             for (int kv = 0; kv < 2; ++kv) {
-              const uint32_t o = kv ? dma_src_v8(w, i, p, rs) : dma_src_k8(w, i, p, rs);
+              const uint32_t o = kv ? dma_src_v8<C>(w, i, p, rs) : dma_src_k8<C>(w, i, p, rs);
               const int row = o / rs;
               CHECK(o % rs + 16 <= (uint32_t)C::rowBytes, "8-bit DMA chunk leaves its row");
               if (t * BN + row < Sk)
@@ -655,6 +653,34 @@ static void check_pingpong(int ntiles, int nw, bool one_barrier) {
 // Replays the four-wave two-block kernel: one group, iteration j issues
 // K(j+2) and V(j+1) (empty ranges past the last tile), reads K(j) and
 // V(j-1), then waits for all but its latest pair and meets the barrier.
+// Interleaved eight-wave schedule (fa_interleave.h): DMA pair j (K(j+2),
+// V(j+1)) is issued at the start of iteration j, before the barrier, so it
+// may run while slower waves are still in iteration j-1; after the barrier
+// of iteration j every pair up to j-1 has landed. Iteration j reads K(j+1)
+// (at the last tile too: S(j+1) is computed and dropped) and V(j); the
+// prologue reads K(0).
+static void check_il_schedule(int ntiles) {
+  const int NS = kStages;
+  int ktile[3] = {0, ntiles > 1 ? 1 : -1, -1}, vtile[3] = {0, -1, -1};
+  int kpair[3] = {-1, -1, -1}, vpair[3] = {-1, -1, -1};  // pair that wrote the stage (-1: prologue)
+  int kread[3] = {-1, -2, -2}, vread[3] = {-2, -2, -2};  // last iteration reading the stage
+  for (int j = 0; j < ntiles; ++j) {
+    const int sk = (j + 2) % NS, sv = (j + 1) % NS;
+    CHECK(kread[sk] <= j - 2, "il: K stage %d refilled at %d while read at %d", sk, j, kread[sk]);
+    CHECK(vread[sv] <= j - 2, "il: V stage %d refilled at %d while read at %d", sv, j, vread[sv]);
+    ktile[sk] = j + 2 < ntiles ? j + 2 : -1;
+    vtile[sv] = j + 1 < ntiles ? j + 1 : -1;
+    kpair[sk] = j;
+    vpair[sv] = j;
+    const int rk = (j + 1) % NS, rv = j % NS;
+    CHECK(kpair[rk] <= j - 1, "il: K stage %d read at %d before its DMA landed", rk, j);
+    if (j + 1 < ntiles) CHECK(ktile[rk] == j + 1, "il: K(%d) not resident at %d", j + 1, j);
+    CHECK(vtile[rv] == j && vpair[rv] <= j - 1, "il: V(%d) not resident at %d", j, j);
+    kread[rk] = j;
+    vread[rv] = j;
+  }
+}
+
 static void check_w2_schedule(int ntiles) {
   const int NS = kStages;
   int ktile[3] = {0, ntiles > 1 ? 1 : -1, -1}, vtile[3] = {0, -1, -1};
@@ -732,18 +758,38 @@ int main() {
   check_global<CfgW2<128>>(2, 16, 8192, true);
   check_global<CfgW2<64>>(10, 64, 1024, false);
   check_global<CfgW2<128>>(1, 1, 65536, true);
-  // 8-bit kernel
-  check_lds8();
+  // interleaved eight-wave kernel (16-bit)
+  check_lds<CfgIL<64>>();
+  check_lds<CfgIL<128>>();
+  for (int ntiles = 1; ntiles <= 40; ++ntiles) check_il_schedule(ntiles);
+  std::printf("interleaved schedule: ntiles 1..40: checked\n");
   for (auto& s : shapes)
-    for (int causal = 0; causal < 2; ++causal) check_global8(s[0], s[1], s[2], s[2], causal);
+    for (int causal = 0; causal < 2; ++causal) {
+      check_global<CfgIL<64>>(s[0], s[1], s[2], causal);
+      check_global<CfgIL<128>>(s[0], s[1], s[2], causal);
+    }
+  check_lengths<CfgIL<64>>();
+  check_lengths<CfgIL<128>>();
+  check_global<CfgIL<128>>(2, 16, 8192, true);
+  // 8-bit kernels (ping-pong with 128-key tiles, interleaved with 64-key tiles)
+  check_lds8<CfgF8>();
+  check_lds8<CfgF8i>();
+  for (auto& s : shapes)
+    for (int causal = 0; causal < 2; ++causal) {
+      check_global8<CfgF8>(s[0], s[1], s[2], s[2], causal);
+      check_global8<CfgF8i>(s[0], s[1], s[2], s[2], causal);
+    }
   {
     const int lens[] = {1, 31, 64, 127, 128, 129, 255, 256, 257, 513};
     for (int lq : lens)
       for (int lk : lens)
-        for (int causal = 0; causal < 2; ++causal)
-          check_global8(1, 2, lq, lk, causal != 0, 128 + 32, 256 + 64);
+        for (int causal = 0; causal < 2; ++causal) {
+          check_global8<CfgF8>(1, 2, lq, lk, causal != 0, 128 + 32, 256 + 64);
+          check_global8<CfgF8i>(1, 2, lq, lk, causal != 0, 128 + 32, 256 + 64);
+        }
   }
-  check_global8(2, 16, 8192, 8192, true);
+  check_global8<CfgF8>(2, 16, 8192, 8192, true);
+  check_global8<CfgF8i>(2, 16, 8192, 8192, true);
   std::printf("8-bit kernel: shapes, length pairs, full size: checked\n");
   if (g_err) {
     std::printf("FAILED with %d errors\n", g_err);
