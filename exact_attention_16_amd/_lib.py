@@ -45,6 +45,7 @@ SIGNATURES = {
     "fa_fwd_diag": (_I, _FWD_ARGS + [_I, _I, _I, _P]),
     "fa_fwd_strided": (_I, [_P] * 5 + [_I] * 6 + [_F, _P, _I, _P]),
     "fa_fwd_varlen": (_I, [_P] * 7 + [_I] * 8 + [_F, _P, _I, _P]),
+    "fa_fwd_kt": (_I, _FWD_ARGS + [_I]),
     "fa_fwd_fp8": (_I, [_P] * 5 + [_I] * 5 + [_F] * 4 + [_P]),
     "fa_fwd_tile": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
                          ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_longlong)]),
@@ -129,6 +130,11 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_
                               max_seqlen_k, total_q, total_k, D, int(causal), scale, stream,
                               dtype, _strides(strides, 9))
     return _check(st, "fa_fwd_varlen") if check else st
+
+
+def fa_fwd_kt(q, kt, v, o, lse, B, H, S, D, causal, scale, stream, dtype, check=True):
+    st = load().fa_fwd_kt(q, kt, v, o, lse, B, H, S, D, int(causal), scale, stream, dtype)
+    return _check(st, "fa_fwd_kt") if check else st
 
 
 def fa_fwd_fp8(q, k, v, o, lse, B, H, S, D, causal, scale, descale_q, descale_k, descale_v,
@@ -313,4 +319,37 @@ def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
     fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                B, H, S, D, causal, float(scale), float(descale_q), float(descale_k),
                float(descale_v), stream.cuda_stream)
+    return out, lse
+
+
+def attention_kt(q, kt, v, causal: bool, scale: float | None = None, out=None, lse=None,
+                 stream=None):
+    """Attention forward with K given transposed.
+
+    q, v: contiguous [B, H, S, D] 16-bit device tensors; kt: contiguous
+    [B, H, D, S] (S a multiple of 8). Returns (o, lse) as :func:`attention`.
+    """
+    import torch
+    if not (q.is_cuda and kt.is_cuda and v.is_cuda):
+        raise ValueError("q, kt, v must be device tensors")
+    if not (q.dtype == kt.dtype == v.dtype):
+        raise ValueError("q, kt, v must share one dtype")
+    B, H, S, D = q.shape
+    if tuple(kt.shape) != (B, H, D, S) or v.shape != q.shape:
+        raise ValueError("kt must be [B, H, D, S] and v [B, H, S, D] for q [B, H, S, D]")
+    if not (q.is_contiguous() and kt.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, kt, v must be contiguous")
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if not (out.is_contiguous() and out.shape == q.shape and lse.is_contiguous()
+            and lse.shape == (B, H, S)):
+        raise ValueError("out must be contiguous [B, H, S, D], lse contiguous [B, H, S]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fa_fwd_kt(q.data_ptr(), kt.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+              B, H, S, D, causal, float(scale), stream.cuda_stream, _dtype_code(q))
     return out, lse

@@ -90,8 +90,11 @@ __device__ __forceinline__ u32x4 lds_tr_pair(const lds_char* p, uint32_t second)
 }
 
 // One wave's share of a work-group: its query rows, accumulators and the
-// per-tile operations on them.
-template <typename T, class C, bool CAUSAL, int THR, bool DIAG>
+// per-tile operations on them. KT: the caller passes K transposed, [D, S]
+// per head (k's "row" stride is then the stride between d rows); a K tile
+// in LDS is then D rows of BN keys, laid out and read like a V tile with
+// the roles of rows and columns swapped (config CK below).
+template <typename T, class C, bool CAUSAL, int THR, bool DIAG, bool KT = false>
 struct Wave {
   static constexpr int D = C::D;
   static constexpr int BN = C::BN;
@@ -101,6 +104,11 @@ struct Wave {
   static constexpr int NKC = BN / 16;  // P.V contraction steps (16 keys each)
   static constexpr int DPW = C::dmaPerWave;
   static constexpr uint32_t RB = C::rowBytes;
+  // a transposed K tile: D rows (d) of BN 16-bit keys, as a V tile of a
+  // configuration with head dimension BN and BN' = D
+  using CK = Cfg<BN, C::NW, D>;
+  static constexpr uint32_t RBK = CK::rowBytes;
+  static_assert(!KT || CK::dmaPerWave == DPW, "a transposed K tile is the same size");
   using Config = C;
   using STile = f32x16[NKB];  // S^T of one KV tile
   using PTile = u32x4[NKC];   // P of one KV tile as P.V operands
@@ -146,7 +154,7 @@ struct Wave {
     rsk = (uint32_t)P.ks * 2u;
     rsv = (uint32_t)P.vs * 2u;
     rso = (uint32_t)P.os * 2u;
-    dsk = (uint32_t)C::dmaRowsK * rsk;
+    dsk = (uint32_t)(KT ? CK::dmaRowsV : C::dmaRowsK) * rsk;
     dsv = (uint32_t)C::dmaRowsV * rsv;
     q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
     qrow = q0w + (lane & 31);
@@ -157,9 +165,9 @@ struct Wave {
     for (int j = 0; j < NDC; ++j)
       qf[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_frag_off<D>(qrow, j, hh, rsq), 0, 0);
     // per-lane LDS / DMA base offsets; the rest are XOR / immediate offsets
-    koff0 = k_read_off<D>(0, 0, lane);
+    koff0 = KT ? v_tr_off<BN>(0, 0, 0, lane) : k_read_off<D>(0, 0, lane);
     voff0 = v_tr_off<D>(0, 0, 0, lane);
-    kdo0 = dma_src_k<C>(wave, 0, lane, rsk);
+    kdo0 = KT ? dma_src_v<CK>(wave, 0, lane, rsk) : dma_src_k<C>(wave, 0, lane, rsk);
     vdo0 = dma_src_v<C>(wave, 0, lane, rsv);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) o[j] = (f32x16){};
@@ -187,14 +195,27 @@ struct Wave {
   // at or past `limit` is an empty range (the DMA then writes zeros)
   __device__ __forceinline__ void dma_k(lds_char* dst, int t, int limit = 0x7fffffff) const {
     const int kv0 = t * BN;
-    const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsk : 0u;
-    const auto r = FA_RSRC(Kh + (size_t)kv0 * rsk, bytes);
+    if constexpr (KT) {
+      // D rows of keys kv0 .. kv0+BN-1; the range runs to the end of this
+      // head's [D, S] block. Keys past Lk read the next row's values (or
+      // zeros past the block): finite, and masked like any key past the end.
+      const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)D * rsk - (uint32_t)kv0 * 2u : 0u;
+      const auto r = FA_RSRC(Kh + (size_t)kv0 * 2, bytes);
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      // (the LDS pointer goes through a local: written inline as the builtin's
-      // argument, the host compilation pass drops the kernel launch stubs)
-      lds_char* const lp = dst + dma_lds_k<C>(wave, i);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, kdo0 + i * dsk, 0, 0, 0);
+      for (int i = 0; i < DPW; ++i) {
+        lds_char* const lp = dst + dma_lds_v<CK>(wave, i);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, kdo0 + i * dsk, 0, 0, 0);
+      }
+    } else {
+      const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsk : 0u;
+      const auto r = FA_RSRC(Kh + (size_t)kv0 * rsk, bytes);
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        // (the LDS pointer goes through a local: written inline as the builtin's
+        // argument, the host compilation pass drops the kernel launch stubs)
+        lds_char* const lp = dst + dma_lds_k<C>(wave, i);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, kdo0 + i * dsk, 0, 0, 0);
+      }
     }
   }
   __device__ __forceinline__ void dma_v(lds_char* dst, int t, int limit = 0x7fffffff) const {
@@ -212,10 +233,19 @@ struct Wave {
   __device__ __forceinline__ void qk(f32x16 (&s)[NKB], const lds_char* kt) const {
 #pragma unroll
     for (int j = 0; j < NDC; ++j) {
-      const lds_char* base = kt + (koff0 ^ (uint32_t)(j << 5));
+      if constexpr (KT) {
+        // K operand of block kb, step j from the transposed tile: the V^T
+        // read of fa_layout.h with d as the row and the key block as jd
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = Ops<T>::mfma(lds16(base + kb * 32 * RB), qf[j], j == 0 ? (f32x16){} : s[kb]);
+        for (int kb = 0; kb < NKB; ++kb)
+          s[kb] = Ops<T>::mfma(lds_tr_pair(kt + (koff0 ^ (uint32_t)(kb << 6)) + j * 16 * RBK, 4 * RBK),
+                               qf[j], j == 0 ? (f32x16){} : s[kb]);
+      } else {
+        const lds_char* base = kt + (koff0 ^ (uint32_t)(j << 5));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          s[kb] = Ops<T>::mfma(lds16(base + kb * 32 * RB), qf[j], j == 0 ? (f32x16){} : s[kb]);
+      }
     }
   }
   // O^T += V^T P^T for the tile at vt
@@ -230,7 +260,10 @@ struct Wave {
   // scheduling patterns of the two products: operands read several MFMAs
   // ahead (two reads per P.V MFMA and one per S MFMA, four MFMAs ahead)
   static __device__ __forceinline__ void pv_schedule() { read_ahead<8, NKC * NDB, 2>(); }
-  static __device__ __forceinline__ void qk_schedule() { read_ahead<4, NDC * NKB, 1>(); }
+  static __device__ __forceinline__ void qk_schedule() {
+    if constexpr (KT) read_ahead<8, NDC * NKB, 2>();
+    else read_ahead<4, NDC * NKB, 1>();
+  }
   // softmax of one tile (about 4.5 vector instructions per score, BN / 2
   // scores per lane) spread over the next tile's S MFMAs
   static __device__ __forceinline__ void il_schedule() {
@@ -339,6 +372,19 @@ __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_pp(const Problem P) {
   pp_body<Wave<T, Cfg8<D>, CAUSAL, THR, DIAG>>(P);
+}
+
+// ------------------------------------------------- K given transposed
+// The ping-pong work-group on a [D, S] K: 64-key tiles at D = 128 and
+// 128-key tiles at D = 64, so that a transposed K tile has 128- or 256-byte
+// rows like a V tile.
+template <int D> using CfgKT = Cfg<D, 8, (D == 64 ? 128 : 64)>;
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_pp_kt(const Problem P) {
+  pp_body<Wave<T, CfgKT<D>, CAUSAL, 8, false, true>>(P);
 }
 
 // ------------------------------------------------- eight waves, interleaved
@@ -680,6 +726,19 @@ static int launch(const Problem& P, int D, int causal, hipStream_t st, int varia
                 : launch_one<T, 128, false, THR, DIAG>(P, st, variant);
 }
 
+template <typename T> static int launch_kt(Problem P, int D, int causal, hipStream_t st) {
+  P.nqt = num_q_tiles(P.Sq, 256);
+  const dim3 grid((unsigned)P.nqt * (unsigned)(P.B * P.H)), block(512);
+  if (D == 64) {
+    if (causal) hipLaunchKernelGGL((fa_fwd_pp_kt<T, 64, true>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((fa_fwd_pp_kt<T, 64, false>), grid, block, 0, st, P);
+  } else {
+    if (causal) hipLaunchKernelGGL((fa_fwd_pp_kt<T, 128, true>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((fa_fwd_pp_kt<T, 128, false>), grid, block, 0, st, P);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 static int launch_dtype(const Problem& P, int D, int causal, int dtype, hipStream_t st) {
   return dtype == FA_BF16 ? launch<__bf16, 8, false>(P, D, causal, st, kAuto)
                           : launch<_Float16, 8, false>(P, D, causal, st, kAuto);
@@ -792,6 +851,40 @@ static int make_fixed(Problem* P, const void* q, const void* k, const void* v, v
                   sv_[] = {st[6], st[7], st[8]}, so_[] = {st[9], st[10], st[11]};
   const long long nl[] = {B, H, Sq}, sl[] = {st[12], st[13], 1};
   return validate_problem(*P, D, nq, sq_, sk_, sv_, so_, nk, 3, nl, sl, 3);
+}
+
+// Dense problem with K given transposed: q, v, o [B,H,S,D], k [B,H,D,S].
+static int make_kt(Problem* P, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int S, int D, int causal, float scale, int dtype, bool* empty) {
+  *empty = false;
+  int r = validate_args(B, H, S, S, D, causal, scale, dtype);
+  if (r != FA_OK) return r;
+  if ((long long)B * H * S == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15)
+    return FA_ERR_ALIGN;
+  if (S % 8) return FA_ERR_ALIGN;  // every row of k (S keys of one d) starts 16-byte aligned
+  if ((long long)S * D * 2 >= (1LL << 31)) return FA_ERR_DIM;
+  const long long n = (long long)B * H * S * D;
+  if (n > (1LL << 40)) return FA_ERR_DIM;
+  const Span sq{(uintptr_t)q, (uintptr_t)q + (uintptr_t)(2 * n)},
+      sk{(uintptr_t)k, (uintptr_t)k + (uintptr_t)(2 * n)},
+      sv{(uintptr_t)v, (uintptr_t)v + (uintptr_t)(2 * n)},
+      so{(uintptr_t)o, (uintptr_t)o + (uintptr_t)(2 * n)},
+      sl{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(4LL * B * H * S)};
+  if (spans_overlap(so, sq) || spans_overlap(so, sk) || spans_overlap(so, sv) ||
+      spans_overlap(sl, sq) || spans_overlap(sl, sk) || spans_overlap(sl, sv) ||
+      spans_overlap(sl, so))
+    return FA_ERR_ALIAS;
+  const long long hs = (long long)S * D;
+  // k's third stride is the distance between its d rows (S elements)
+  *P = Problem{q, k, v, o, lse, H * hs, hs, D, H * hs, hs, S, H * hs, hs, D, H * hs, hs, D,
+               (long long)H * S, S, nullptr, nullptr, 0, 0, B, H, S, S, 0, scale * kLog2e,
+               nullptr};
+  return FA_OK;
 }
 
 // 8-bit inputs (fa_fwd_fp8.hip)
@@ -958,6 +1051,16 @@ const char* fa_strerror(int status) {
     case FA_ERR_LAYOUT: return "a stride is negative, a row stride is below D, or output rows overlap";
     default: return "unknown status";
   }
+}
+
+int fa_fwd_kt(const void* q, const void* kt, const void* v, void* o, float* lse, int B, int H,
+              int S, int D, int causal, float scale, hipStream_t stream, int dtype) {
+  fa::Problem P;
+  bool empty;
+  const int r = fa::make_kt(&P, q, kt, v, o, lse, B, H, S, D, causal, scale, dtype, &empty);
+  if (r != FA_OK || empty) return r;
+  return dtype == FA_BF16 ? fa::launch_kt<__bf16>(P, D, causal, stream)
+                          : fa::launch_kt<_Float16>(P, D, causal, stream);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

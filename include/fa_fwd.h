@@ -203,6 +203,27 @@ int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n,
                 int* threads, long long* work_groups);
 
 /*
+ * fa_fwd_kt -- fa_fwd with K given transposed: "FlashAttention的Triton性能
+ * 考古学" (hotdry.top, section "解决方案：预转置 K 矩阵") stores K^T so that
+ * the Q K^T tiles read contiguous memory.
+ *
+ *   kt       device, [B,H,D,S] of `dtype` (for each (b, h), D rows of S
+ *            keys: element (b, h, d, j) at kt + ((b*H + h)*D + d)*S + j),
+ *            16-byte aligned, read only
+ *   S        a multiple of 8 (each d row starts 16-byte aligned), else
+ *            FA_ERR_ALIGN; B*H*S == 0 is a no-op
+ *   q, v, o, lse and the other arguments as for fa_fwd (q, v, o [B,H,S,D]).
+ *
+ * The result equals fa_fwd's on the same values (up to the rounding order
+ * of the row sums: the kernel uses 64-key tiles at D = 128 and 128-key
+ * tiles at D = 64). Errors as for fa_fwd; o or lse overlapping kt:
+ * FA_ERR_ALIAS.
+ */
+int fa_fwd_kt(const void* q, const void* kt, const void* v, void* o, float* lse,
+              int B, int H, int S, int D, int causal, float scale,
+              hipStream_t stream, int dtype);
+
+/*
  * fa_fwd_fp8 -- fa_fwd on 8-bit float inputs with one descale per tensor:
  * the FP8 support that "FlashAttention的Triton性能考古学" (hotdry.top,
  * section "架构感知优化策略") lists for newer GPUs.

@@ -24,8 +24,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == {"fa_fwd", "fa_fwd_f16", "fa_fwd_bf16", "fa_fwd_diag",
-                           "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_tile",
-                           "fa_strerror", "fa_version"}
+                           "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_kt", "fa_fwd_fp8",
+                           "fa_fwd_tile", "fa_strerror", "fa_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,8 +49,9 @@ def test_kernel_launch_stubs_are_defined():
     out = subprocess.run([nm, "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
     stubs = [l for l in out.splitlines() if "device_stub" in l]
     # 4 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic
-    # thresholds), and the 8-bit kernel x 2 masks
-    assert len(stubs) == 98
+    # thresholds), the transposed-K kernel x 2 dtypes x 2 head dims x 2 masks,
+    # and the 8-bit kernel x 2 masks
+    assert len(stubs) == 106
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
@@ -279,3 +280,26 @@ def test_fp8_empty_problem_is_a_noop():
     assert _call8(S=0) == OK
     assert _call8(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
     assert _call8(H=0, D=64) == UNSUP  # the head dimension is checked first
+
+
+# ------------------------------------------------ K given transposed
+def _call_kt(**kw):
+    a = dict(GOOD, S=104)
+    a.update(kw)
+    return fa.fa_fwd_kt(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["D"],
+                        a["causal"], a["scale"], a["stream"], a["dtype"], check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=0), NULL), (dict(lse=0), NULL), (dict(B=-1), DIM), (dict(D=96), UNSUP),
+    (dict(dtype=3), UNSUP), (dict(S=100), ALIGN), (dict(S=7), ALIGN), (dict(k=K + 8), ALIGN),
+    (dict(scale=0.0), SCALE), (dict(o=K + 64), ALIAS), (dict(lse=O + 32), ALIAS),
+    (dict(causal=3), ARG),
+])
+def test_kt_validation_rejects(kw, expect):
+    assert _call_kt(**kw) == expect
+
+
+def test_kt_empty_problem_is_a_noop():
+    assert _call_kt(S=0) == OK
+    assert _call_kt(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
