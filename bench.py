@@ -288,7 +288,9 @@ def main(argv=None) -> int:
                 "frac": tflops / PEAK_TFLOPS, "traffic": traffic,
                 "kernel": kernel_name(w),
                 "flops_per_launch": w.flops, "avg_launch_ms": ms_per_step,
-                "median_launch_ms": med_ms, "algorithmic_bytes_per_launch": bytes_alg}
+                "median_launch_ms": med_ms, "algorithmic_bytes_per_launch": bytes_alg,
+                "algorithmic_gbs": bytes_alg / (ms_per_step * 1e-3) / 1e9,
+                "hbm_gbs": traffic / (ms_per_step * 1e-3) / 1e9 if traffic else None}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -380,7 +382,8 @@ def bench_fp8(args, torch, fa, w) -> int:
                 "kernel": f"fa_fwd_il8<causal={int(w.causal)}> ({groups} work-groups x 512 "
                           f"threads, 256 query rows, 64-key tiles)",
                 "flops_per_launch": w.flops, "avg_launch_ms": ms, "median_launch_ms": med,
-                "algorithmic_bytes_per_launch": w.algorithmic_bytes}
+                "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+                "algorithmic_gbs": w.algorithmic_bytes / (ms * 1e-3) / 1e9}
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, qc, kc, vc, descale=ds)
     out = {
         "metric": "attention fwd TFLOPS (B·H·S²·D·4, causal halved) + % of fp8 MFMA peak",
