@@ -176,7 +176,10 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *                    shape, 1 = the four-wave kernel (128 query rows per
  *                    work-group), 2 = the eight-wave ping-pong kernel (256
  *                    rows), 3 = the four-wave kernel with two 32-row blocks
- *                    per wave (256 rows, 32-key tiles). Every variant
+ *                    per wave (256 rows, 32-key tiles), 4 = the eight-wave
+ *                    kernel in which every wave overlaps its own softmax
+ *                    with its next tile's MFMAs (256 rows, 64-key tiles;
+ *                    the "interleaved" kernel). Every variant
  *                    computes the same result, to rounding; the choice only
  *                    affects speed.
  * It runs separate, instrumented instantiations of the same kernels.
