@@ -379,8 +379,8 @@ def bench_fp8(args, torch, fa, w) -> int:
     groups = w.B * w.H * -(-w.S // 256)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS_FP8, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_TFLOPS_FP8, "traffic": load_traffic(w.name),
-                "kernel": f"fa_fwd_il8<causal={int(w.causal)}> ({groups} work-groups x 512 "
-                          f"threads, 256 query rows, 64-key tiles)",
+                "kernel": f"fa_fwd_il8<D={w.D},causal={int(w.causal)}> ({groups} work-groups x "
+                          f"512 threads, 256 query rows, {64 if w.D == 128 else 128}-key tiles)",
                 "flops_per_launch": w.flops, "avg_launch_ms": ms, "median_launch_ms": med,
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes,
                 "algorithmic_gbs": w.algorithmic_bytes / (ms * 1e-3) / 1e9}

@@ -291,7 +291,7 @@ def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
     """Attention forward on 8-bit float inputs with per-tensor descales.
 
     q, k, v: contiguous [B, H, S, D] device tensors of E4M3 codes
-    (torch.float8_e4m3fn, or uint8 holding the codes), D = 128; the value of
+    (torch.float8_e4m3fn, or uint8 holding the codes), D = 64 or 128; the value of
     a code is its E4M3 value times the tensor's descale. Returns (o, lse):
     o [B, H, S, D] bfloat16, lse [B, H, S] float32, enqueued on `stream`
     (default: torch's current stream) without synchronising.

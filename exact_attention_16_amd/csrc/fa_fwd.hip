@@ -888,7 +888,7 @@ static int make_kt(Problem* P, const void* q, const void* k, const void* v, void
 }
 
 // 8-bit inputs (fa_fwd_fp8.hip)
-int launch_fp8(Problem P, int causal, hipStream_t stream);
+int launch_fp8(Problem P, int D, int causal, hipStream_t stream);
 
 static bool positive_finite(float x) { return x > 0.f && isfinite(x); }
 
@@ -900,7 +900,7 @@ static int make_fp8(Problem* P, const void* q, const void* k, const void* v, voi
   *empty = false;
   if (B < 0 || H < 0 || S < 0) return FA_ERR_DIM;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  if (D != 128) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (!positive_finite(scale) || !positive_finite(dq) || !positive_finite(dk) ||
       !positive_finite(dv))
     return FA_ERR_SCALE;
@@ -1071,7 +1071,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   const int r = fa::make_fp8(&P, q, k, v, o, lse, B, H, S, D, causal, scale, descale_q,
                              descale_k, descale_v, &empty);
   if (r != FA_OK || empty) return r;
-  return fa::launch_fp8(P, causal, stream);
+  return fa::launch_fp8(P, D, causal, stream);
 }
 
 int fa_version(void) { return 310; }

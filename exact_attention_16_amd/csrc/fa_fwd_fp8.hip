@@ -4,9 +4,10 @@
 //
 // Work-group: eight waves of 32 query rows (fa_interleave.h), each
 // overlapping the softmax of KV tile j with the MFMAs of tile j+1's scores,
-// K/V in three LDS stages filled by direct DMA, 64-key tiles. Both products
+// K/V in three LDS stages filled by direct DMA, 64-key tiles (128 at
+// D = 64). Both products
 // use the 8-bit matrix instruction v_mfma_f32_32x32x64_f8f6f4:
-//   S^T = K Q^T   two 64-deep steps per 32-key block (D = 128)
+//   S^T = K Q^T   one 64-deep step per 32-key block per 64 of D
 //   O^T += V^T P^T  one 64-key chunk per MFMA, P rounded to E4M3
 // The operand layouts (fa_layout8.h) put each lane's 32 S values of a 64-key
 // chunk in key order, so P packs straight into the P.V operand
@@ -29,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "../../include/fa_fwd.h"
 #include "fa_device.h"
@@ -129,8 +132,8 @@ struct Wave8 {
       const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rq, q8_frag_off(qrow, j, hh, 1, rsq), 0, 0);
       qf[j] = (u32x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
-    koff0 = k8_read_off(0, 0, 0, lane);
-    voff0 = v8_tr_off(0, 0, 0, lane);
+    koff0 = k8_read_off<D>(0, 0, 0, lane);
+    voff0 = v8_tr_off<D>(0, 0, 0, lane);
     kdo0 = dma_src_k8<C>(wave, 0, lane, rsk);
     vdo0 = dma_src_v8<C>(wave, 0, lane, rsv);
 #pragma unroll
@@ -293,24 +296,33 @@ struct Wave8 {
   }
 };
 
-template <bool CAUSAL>
+// 64-key tiles at D = 128; at D = 64 a 64-key tile would be less than one
+// 1-KiB DMA issue per wave, so 128-key tiles
+template <int D> using CfgF8il = typename std::conditional<D == 64, CfgF8h, CfgF8i>::type;
+
+template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_il8(const Problem P) {
-  il_body<Wave8<CAUSAL, 2, CfgF8i>>(P);
+  il_body<Wave8<CAUSAL, 2, CfgF8il<D>>>(P);
 }
 
 // Launches the 8-bit kernel for a filled, validated Problem. (The same wave
 // type also runs under the ping-pong body, pp_body<Wave8<CAUSAL, 2>> with
-// 128-key tiles; on the long causal workload that took 5% longer.)
-int launch_fp8(Problem P, int causal, hipStream_t stream) {
-  P.nqt = num_q_tiles(P.Sq, CfgF8i::BM);
-  const dim3 grid((unsigned)P.nqt * (unsigned)(P.B * P.H)), block(CfgF8i::threads);
+// 128-key tiles; on the long causal workload at D = 128 that took 5%
+// longer.)
+template <int D> static int launch_fp8_d(Problem P, int causal, hipStream_t stream) {
+  P.nqt = num_q_tiles(P.Sq, CfgF8il<D>::BM);
+  const dim3 grid((unsigned)P.nqt * (unsigned)(P.B * P.H)), block(CfgF8il<D>::threads);
   if (causal)
-    hipLaunchKernelGGL(fa_fwd_il8<true>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((fa_fwd_il8<D, true>), grid, block, 0, stream, P);
   else
-    hipLaunchKernelGGL(fa_fwd_il8<false>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((fa_fwd_il8<D, false>), grid, block, 0, stream, P);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int launch_fp8(Problem P, int D, int causal, hipStream_t stream) {
+  return D == 64 ? launch_fp8_d<64>(P, causal, stream) : launch_fp8_d<128>(P, causal, stream);
 }
 
 }  // namespace fa

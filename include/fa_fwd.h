@@ -241,7 +241,7 @@ int fa_fwd_kt(const void* q, const void* kt, const void* v, void* o, float* lse,
  *            likewise for k and v; finite and > 0. The output is attention
  *            of those values: o and lse as fa_fwd defines them with
  *            x_ij = scale * descale_q * descale_k * <q_i, k_j>.
- *   D        128 only (FA_ERR_UNSUPPORTED otherwise)
+ *   D        64 or 128 (FA_ERR_UNSUPPORTED otherwise)
  *   other arguments as for fa_fwd; any S >= 1; B*H*S == 0 is a no-op.
  *
  * Precision: the logits and the row sums are exact products accumulated in

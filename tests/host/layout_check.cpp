@@ -348,7 +348,7 @@ template <class C> static std::vector<long> dma_tile8(bool is_k, int* worst64) {
         CHECK(dst % 16 == 0 && dst + 16 <= (uint32_t)C::tileBytes, "DMA dst %u", dst);
         CHECK(src % 16 == 0 && src + 16 <= (uint32_t)C::tileBytes, "DMA src %u", src);
         const int row = src / C::rowBytes, d0 = src % C::rowBytes;
-        const uint32_t expect = is_k ? k8_off(row, d0 / 16) : v8_off(row, d0 / 16);
+        const uint32_t expect = is_k ? k8_off<C::D>(row, d0 / 16) : v8_off<C::D>(row, d0 / 16);
         CHECK(expect == dst, "8-bit DMA slot mismatch w=%d i=%d p=%d", w, i, p);
         for (int e = 0; e < 16; ++e) {
           CHECK(tag[dst + e] == -1, "LDS byte %u written twice", dst + e);
@@ -374,8 +374,8 @@ template <class C> static void check_lds8() {
       for (int x = 0; x < 2; ++x) {
         std::vector<uint32_t> addr(64);
         for (int lane = 0; lane < 64; ++lane) {
-          const uint32_t off = k8_read_off(kb, j, x, lane);
-          CHECK(off == (k8_read_off(0, 0, 0, lane) ^ (uint32_t)(j << 6 | x << 4)) +
+          const uint32_t off = k8_read_off<D>(kb, j, x, lane);
+          CHECK(off == (k8_read_off<D>(0, 0, 0, lane) ^ (uint32_t)(j << 6 | x << 4)) +
                            k8_block_rows(kb) * (uint32_t)C::rowBytes,
                 "k8_read_off is not step 0 XOR (j << 6 | x << 4) plus the block's rows");
           addr[lane] = off;
@@ -397,8 +397,8 @@ template <class C> static void check_lds8() {
         std::vector<uint32_t> addr(64);
         long src[64][8];
         for (int lane = 0; lane < 64; ++lane) {
-          const uint32_t off = v8_tr_off(jd, c, t, lane);
-          CHECK(off == (v8_tr_off(0, 0, 0, lane) ^ (uint32_t)(jd << 5)) +
+          const uint32_t off = v8_tr_off<D>(jd, c, t, lane);
+          CHECK(off == (v8_tr_off<D>(0, 0, 0, lane) ^ (uint32_t)(jd << 5)) +
                            (uint32_t)((64 * c + 8 * t) * C::rowBytes),
                 "v8_tr_off is not block 0 XOR (jd << 5) plus 64c + 8t rows");
           addr[lane] = off;
@@ -447,8 +447,8 @@ template <class C> static void check_lds8() {
 // Global accesses of the 8-bit kernel for B*H heads of Sq x Sk: rows rs
 // bytes apart in q, k, v and rso bytes apart in o (16-bit output).
 template <class C>
-static void check_global8(int B, int H, int Sq, int Sk, bool causal, uint32_t rs = 128,
-                          uint32_t rso = 256) {
+static void check_global8(int B, int H, int Sq, int Sk, bool causal, uint32_t rs = C::rowBytes,
+                          uint32_t rso = 2 * C::D) {
   const int BH = B * H, nqt = num_q_tiles(Sq, C::BM), BN = C::BN;
   const long grid = (long)nqt * BH;
   const uint32_t q_bytes = (uint32_t)Sq * rs, o_bytes = (uint32_t)Sq * rso;
@@ -774,10 +774,12 @@ int main() {
   // 8-bit kernels (ping-pong with 128-key tiles, interleaved with 64-key tiles)
   check_lds8<CfgF8>();
   check_lds8<CfgF8i>();
+  check_lds8<CfgF8h>();
   for (auto& s : shapes)
     for (int causal = 0; causal < 2; ++causal) {
       check_global8<CfgF8>(s[0], s[1], s[2], s[2], causal);
       check_global8<CfgF8i>(s[0], s[1], s[2], s[2], causal);
+      check_global8<CfgF8h>(s[0], s[1], s[2], s[2], causal);
     }
   {
     const int lens[] = {1, 31, 64, 127, 128, 129, 255, 256, 257, 513};
@@ -786,10 +788,12 @@ int main() {
         for (int causal = 0; causal < 2; ++causal) {
           check_global8<CfgF8>(1, 2, lq, lk, causal != 0, 128 + 32, 256 + 64);
           check_global8<CfgF8i>(1, 2, lq, lk, causal != 0, 128 + 32, 256 + 64);
+          check_global8<CfgF8h>(1, 2, lq, lk, causal != 0, 64 + 48, 128 + 16);
         }
   }
   check_global8<CfgF8>(2, 16, 8192, 8192, true);
   check_global8<CfgF8i>(2, 16, 8192, 8192, true);
+  check_global8<CfgF8h>(10, 64, 1024, 1024, false);
   std::printf("8-bit kernel: shapes, length pairs, full size: checked\n");
   if (g_err) {
     std::printf("FAILED with %d errors\n", g_err);

@@ -50,8 +50,8 @@ def test_kernel_launch_stubs_are_defined():
     stubs = [l for l in out.splitlines() if "device_stub" in l]
     # 4 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic
     # thresholds), the transposed-K kernel x 2 dtypes x 2 head dims x 2 masks,
-    # and the 8-bit kernel x 2 masks
-    assert len(stubs) == 106
+    # and the 8-bit kernel x 2 head dims x 2 masks
+    assert len(stubs) == 108
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
@@ -261,7 +261,7 @@ NBYTES = 2 * 3 * 100 * 128  # one 8-bit input tensor of GOOD8
     (dict(q=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL),
     (dict(B=-1), DIM), (dict(S=-1), DIM), (dict(S=1 << 23), DIM),
     (dict(B=1 << 16, H=1 << 16, S=1 << 12), DIM),
-    (dict(D=64), UNSUP), (dict(D=256), UNSUP),
+    (dict(D=96), UNSUP), (dict(D=256), UNSUP),
     (dict(k=K + 8), ALIGN), (dict(lse=L + 4), ALIGN),
     (dict(scale=0.0), SCALE), (dict(dq=0.0), SCALE), (dict(dk=-1.0), SCALE),
     (dict(dv=float("nan")), SCALE), (dict(dv=float("inf")), SCALE),
@@ -279,7 +279,7 @@ def test_fp8_validation_rejects(kw, expect):
 def test_fp8_empty_problem_is_a_noop():
     assert _call8(S=0) == OK
     assert _call8(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
-    assert _call8(H=0, D=64) == UNSUP  # the head dimension is checked first
+    assert _call8(H=0, D=96) == UNSUP  # the head dimension is checked first
 
 
 # ------------------------------------------------ K given transposed

@@ -70,14 +70,15 @@ def _run(codes, ds, causal, scale=None):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,S", [(1, 2, 128), (1, 2, 200), (2, 3, 300), (1, 1, 1),
                                    (1, 2, 513), (1, 1, 1024), (1, 1, 257)])
-def test_fp8_all_rows(B, H, S, causal):
-    tag = f"fp8 B={B} H={H} S={S} causal={causal}"
+def test_fp8_all_rows(B, H, S, causal, D):
+    tag = f"fp8 B={B} H={H} S={S} D={D} causal={causal}"
     _banner(tag)
-    codes, ds = _inputs((B, H, S, 128), 7000 + S + causal)
-    scale = float(np.float32(1 / math.sqrt(128)))
+    codes, ds = _inputs((B, H, S, D), 7000 + S + causal + D)
+    scale = float(np.float32(1 / math.sqrt(D)))
     og, lg = _run(codes, ds, causal)
     worst = (0.0, 0.0, 0.0)
     for b in range(B):
@@ -132,6 +133,21 @@ def test_fp8_full_size_sampled_rows():
             f"max|dlse|={worst[2]:.3e}")
     assert worst[0] <= 1.0 and worst[2] <= LSE_TOL, worst
     assert np.isfinite(og).all() and np.isfinite(lg).all()
+
+
+def test_fp8_head_dim_64_full_size_sampled_rows():
+    """The batched non-causal shape (10 x 64 heads x 1024 x 64) in 8-bit."""
+    w = W.WORKLOADS["bat8"]
+    _banner(f"fp8 full size {w.B}x{w.H}x{w.S}x{w.D}")
+    codes, ds = W.make_fp8_inputs(w)
+    og, lg = _run(codes, ds, w.causal)
+    worst = (0.0, 0.0, 0.0)
+    for b, h in [(0, 0), (3, 17), (9, 63)]:
+        rows = sample_rows(w.S, 24, seed=100 + b * 64 + h, block_m=256)
+        r = _check_head(codes, ds, og, lg, b, h, rows, w.causal, w.scale, "bat8")
+        worst = tuple(max(x, y) for x, y in zip(worst, r))
+    _banner(f"fp8 D=64 full size: max |dO|/tol={worst[0]:.3f} max|dlse|={worst[2]:.3e}")
+    assert worst[0] <= 1.0 and worst[2] <= LSE_TOL, worst
 
 
 def test_fp8_stream_and_repeat_are_deterministic():

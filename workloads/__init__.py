@@ -20,6 +20,7 @@ long  2, 16, 8192, 128                  bf16   yes     long-context causal
 ramp  1, 8, 16384, 128                  bf16   yes     rescale stress (key ramp)
 long8 2, 16, 8192, 128                  e4m3   yes     the long workload in 8-bit
                                                        floats, per-tensor scales
+bat8  10, 64, 1024, 64                  e4m3   no      the bat workload in 8-bit
 ====  ================================  =====  ======  ==========================
 
 Recipe: ``numpy.random.default_rng(seed)`` draws Q, then K, then V as float32
@@ -93,6 +94,7 @@ WORKLOADS = {
     "long": Workload("long", 2, 16, 8192, 128, BF16, True, 4),
     "ramp": Workload("ramp", 1, 8, 16384, 128, BF16, True, 5, ramp=0.002),
     "long8": Workload("long8", 2, 16, 8192, 128, E4M3, True, 4),
+    "bat8": Workload("bat8", 10, 64, 1024, 64, E4M3, False, 3),
 }
 
 
