@@ -185,6 +185,79 @@ __device__ __forceinline__ HeadRows head_rows(const Problem& P, int bb, int h) {
   return r;
 }
 
+// What every wave type knows about its rows (configuration C, causal mask,
+// base lag THR in log2 units): which 32 query rows it owns, its sequence's
+// lengths, the running base b of the online softmax and its share of the
+// row sum, and the decisions that follow from them (tile counts, whether a
+// tile needs index compares, the base update).
+template <class C, bool CAUSAL, int THR> struct RowState {
+  int lane, wave, hh, q0w, qrow, qt;
+  int Lq, Lk, off;  // this sequence's query and key rows; off = Lk - Lq (causal alignment)
+  float c;          // base-2 multiplier of the raw dot products
+  float b, lsum;    // running base (log2 units, lags the true max by <= THR);
+                    // this lane's partial row sum (its k-half of the keys)
+
+  // Finds this wave's rows (sub: which 32-row block of the wave's C::RPW
+  // rows) and its sequence; false when the work-group's query tile lies
+  // wholly past the sequence's end (the same for every wave of the
+  // work-group, which then returns before any DMA or barrier).
+  __device__ __forceinline__ bool locate(const Problem& P, int sub, HeadRows* hr) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    hh = lane >> 5;
+    c = P.c;
+    int bh;
+    block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh);
+    const int bb = bh / P.H, h = bh - bb * P.H;
+    *hr = head_rows(P, bb, h);
+    Lq = hr->Lq;
+    Lk = hr->Lk;
+    if (qt * C::BM >= Lq) return false;
+    off = Lk - Lq;
+    q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
+    qrow = q0w + (lane & 31);
+    return true;
+  }
+  __device__ __forceinline__ void reset_softmax() {
+    b = -INFINITY;
+    lsum = 0.f;
+  }
+
+  // KV tiles this wave computes (0 for a wave wholly past the end), and the
+  // work-group's KV tile count.
+  __device__ __forceinline__ int wave_tiles() const {
+    return q0w < Lq ? (wave_kv_end(q0w, Lq, Lk, CAUSAL) + C::BN - 1) / C::BN : 0;
+  }
+  __device__ __forceinline__ int group_tiles() const {
+    return (tile_kv_end(qt, Lq, Lk, CAUSAL, C::BM) + C::BN - 1) / C::BN;
+  }
+  // Leading KV tiles that need no index compares for these rows
+  __device__ __forceinline__ int unmasked_tiles() const {
+    return fa::unmasked_tiles(q0w, Lq, Lk, CAUSAL, C::BN);
+  }
+  // the tile starting at key kv0 needs index compares (diagonal or ragged end)
+  __device__ __forceinline__ bool needs_mask(int kv0) const {
+    return (CAUSAL && kv0 + C::BN - 1 > q0w + off) || kv0 + C::BN > Lk;
+  }
+  // running max with lag over one tile's scores (each lane holds 16 per
+  // 32-key block): new base b and history factor 2^(b_old - b_new)
+  template <int NKB> __device__ __forceinline__ float softmax_max(const f32x16 (&s)[NKB]) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
+    mx = max_xor32(mx);
+    const float cand = vmax(b, mx * c);
+    const bool rebase = cand > b + (float)THR;
+    const float hist = rebase ? __builtin_amdgcn_exp2f(b - cand) : 1.f;  // 0 on the first tile
+    b = rebase ? cand : b;
+    lsum *= hist;
+    return hist;
+  }
+};
+
 template <int R, class X> __device__ __forceinline__ X pick3(X a, X b, X c) {
   if constexpr (R == 0) return a;
   else if constexpr (R == 1) return b;

@@ -95,7 +95,10 @@ __device__ __forceinline__ u32x4 lds_tr_pair(const lds_char* p, uint32_t second)
 // in LDS is then D rows of BN keys, laid out and read like a V tile with
 // the roles of rows and columns swapped (config CK below).
 template <typename T, class C, bool CAUSAL, int THR, bool DIAG, bool KT = false>
-struct Wave {
+struct Wave : RowState<C, CAUSAL, THR> {
+  using Rows = RowState<C, CAUSAL, THR>;
+  using Rows::lane, Rows::wave, Rows::hh, Rows::q0w, Rows::qrow, Rows::qt, Rows::Lq, Rows::Lk,
+      Rows::off, Rows::c, Rows::b, Rows::lsum;
   static constexpr int D = C::D;
   static constexpr int BN = C::BN;
   static constexpr int NKB = BN / 32;  // 32-key blocks per KV tile
@@ -113,10 +116,7 @@ struct Wave {
   using STile = f32x16[NKB];  // S^T of one KV tile
   using PTile = u32x4[NKC];   // P of one KV tile as P.V operands
 
-  int lane, wave, hh, q0w, qrow, qt;
-  int Lq, Lk, off;  // this sequence's query and key rows; off = Lk - Lq (causal alignment)
-  float c;          // scale * log2(e)
-  const char* Kh;   // row 0 of this (sequence, head) in k, v, o, lse
+  const char* Kh;  // row 0 of this (sequence, head) in k, v, o, lse
   const char* Vh;
   char* Oh;
   float* Lh;
@@ -125,28 +125,15 @@ struct Wave {
   uint32_t koff0, voff0, kdo0, vdo0;
   u32x4 qf[NDC];
   f32x16 o[NDB];
-  float b, lsum;
   unsigned n_events;
 
-  // Sets up this wave's rows of the work-group's query tile; false when the
-  // tile lies wholly past its sequence's end (the same for every wave of the
-  // work-group, which then returns before any DMA or barrier).
-  // sub: which 32-row block of the wave's C::RPW rows this object holds
+  // Sets up this wave's rows of the work-group's query tile (see
+  // RowState::locate); false when the tile lies wholly past its sequence's
+  // end. sub: which 32-row block of the wave's C::RPW rows this object holds
   __device__ __forceinline__ bool init(const Problem& P, int sub = 0) {
-    const int tid = threadIdx.x;
-    lane = tid & 63;
-    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    hh = lane >> 5;
-    c = P.c;
-    int bh;
-    block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh);
-    const int bb = bh / P.H, h = bh - bb * P.H;
-    const HeadRows hr = head_rows(P, bb, h);
-    Lq = hr.Lq;
-    Lk = hr.Lk;
+    HeadRows hr;
+    if (!this->locate(P, sub, &hr)) return false;
     const long long q0 = hr.q0, k0 = hr.k0, v0 = hr.v0, o0 = hr.o0, l0 = hr.l0;
-    if (qt * C::BM >= Lq) return false;
-    off = Lk - Lq;
     Kh = (const char*)P.k + k0 * 2;
     Vh = (const char*)P.v + v0 * 2;
     Oh = (char*)P.o + o0 * 2;
@@ -156,8 +143,6 @@ struct Wave {
     rso = (uint32_t)P.os * 2u;
     dsk = (uint32_t)(KT ? CK::dmaRowsV : C::dmaRowsK) * rsk;
     dsv = (uint32_t)C::dmaRowsV * rsv;
-    q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
-    qrow = q0w + (lane & 31);
     // Q operand fragments (rows past Lq read as zeros)
     const uint32_t rsq = (uint32_t)P.qs * 2u;
     const auto rq = FA_RSRC((const char*)P.q + q0 * 2, (uint32_t)Lq * rsq);
@@ -171,24 +156,9 @@ struct Wave {
     vdo0 = dma_src_v<C>(wave, 0, lane, rsv);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) o[j] = (f32x16){};
-    b = -INFINITY;  // running base, log2 units (lags the true max by <= THR)
-    lsum = 0.f;     // this lane's partial row sum (its k-half of the keys)
+    this->reset_softmax();
     n_events = 0;
     return true;
-  }
-
-  // KV tiles this wave computes (0 for a wave wholly past the end), and the
-  // work-group's KV tile count.
-  __device__ __forceinline__ int wave_tiles() const {
-    return q0w < Lq ? (wave_kv_end(q0w, Lq, Lk, CAUSAL) + BN - 1) / BN : 0;
-  }
-  __device__ __forceinline__ int group_tiles() const {
-    return (tile_kv_end(qt, Lq, Lk, CAUSAL, C::BM) + BN - 1) / BN;
-  }
-
-  // Leading KV tiles that need no index compares for these rows
-  __device__ __forceinline__ int unmasked_tiles() const {
-    return fa::unmasked_tiles(q0w, Lq, Lk, CAUSAL, BN);
   }
 
   // this wave's share of the DMA of K or V tile t into an LDS stage; a tile
@@ -269,10 +239,6 @@ struct Wave {
   static __device__ __forceinline__ void il_schedule() {
     mix<4, NDC * NKB, 1, (9 * BN / 4) / (NDC * NKB) + 1>();
   }
-  // the tile starting at key kv0 needs index compares (diagonal or ragged end)
-  __device__ __forceinline__ bool needs_mask(int kv0) const {
-    return (CAUSAL && kv0 + BN - 1 > q0w + off) || kv0 + BN > Lk;
-  }
   __device__ __forceinline__ void mask(f32x16 (&s)[NKB], int kv0) const {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -282,21 +248,6 @@ struct Wave {
         const bool vis = key < Lk && (!CAUSAL || key <= qrow + off);
         s[kb][r] = vis ? s[kb][r] : -INFINITY;
       }
-  }
-  // running max with lag: new base b and history factor 2^(b_old - b_new)
-  __device__ __forceinline__ float softmax_max(const f32x16 (&s)[NKB]) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
-    mx = max_xor32(mx);
-    const float cand = vmax(b, mx * c);
-    const bool rebase = cand > b + (float)THR;
-    const float hist = rebase ? __builtin_amdgcn_exp2f(b - cand) : 1.f;  // 0 on the first tile
-    b = rebase ? cand : b;
-    lsum *= hist;
-    return hist;
   }
   // p = 2^(s*c - b), row sum of the unrounded p, P packed for the P.V MFMA
   __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[NKB], u32x4 (&p)[NKC]) {
@@ -328,8 +279,8 @@ struct Wave {
   // softmax of tile j in place: mask, base update, rescale of O, P(j)
   __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NKB], u32x4 (&p)[NKC], int j) {
     const int kv0 = j * BN;
-    if (needs_mask(kv0)) mask(s, kv0);
-    const float hist = softmax_max(s);
+    if (this->needs_mask(kv0)) mask(s, kv0);
+    const float hist = this->softmax_max(s);
     rescale(j, hist);
     softmax_exp(s, p);
   }

@@ -68,7 +68,10 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 // One wave's 32 query rows of the 8-bit kernel (the interface il_body and
 // pp_body use).
 template <bool CAUSAL, int THR, class C_ = CfgF8>
-struct Wave8 {
+struct Wave8 : RowState<C_, CAUSAL, THR> {
+  using Rows = RowState<C_, CAUSAL, THR>;
+  using Rows::lane, Rows::wave, Rows::hh, Rows::q0w, Rows::qrow, Rows::qt, Rows::Lq, Rows::Lk,
+      Rows::off, Rows::c, Rows::b, Rows::lsum;
   using C = C_;
   using Config = C_;
   static constexpr int D = C::D;
@@ -83,9 +86,7 @@ struct Wave8 {
   using STile = f32x16[NKB];
   using PTile = u32x8[NCH];
 
-  int lane, wave, hh, q0w, qrow, qt;
-  int Lq, Lk, off;
-  float c, vscale;
+  float vscale;
   const char* Kh;
   const char* Vh;
   char* Oh;
@@ -95,23 +96,11 @@ struct Wave8 {
   uint32_t koff0, voff0, kdo0, vdo0;
   u32x8 qf[NDJ];
   f32x16 o[NDB];
-  float b, lsum;
 
   __device__ __forceinline__ bool init(const Problem& P) {
-    const int tid = threadIdx.x;
-    lane = tid & 63;
-    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    hh = lane >> 5;
-    c = P.c;
+    HeadRows hr;
+    if (!this->locate(P, 0, &hr)) return false;
     vscale = P.vscale;
-    int bh;
-    block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh);
-    const int bb = bh / P.H, h = bh - bb * P.H;
-    const HeadRows hr = head_rows(P, bb, h);
-    Lq = hr.Lq;
-    Lk = hr.Lk;
-    if (qt * C::BM >= Lq) return false;
-    off = Lk - Lq;
     // one-byte Q, K, V elements; two-byte O elements
     Kh = (const char*)P.k + hr.k0;
     Vh = (const char*)P.v + hr.v0;
@@ -122,8 +111,6 @@ struct Wave8 {
     rso = (uint32_t)P.os * 2u;
     dsk = (uint32_t)C::dmaRowsK * rsk;
     dsv = (uint32_t)C::dmaRowsV * rsv;
-    q0w = qt * C::BM + wave * C::RPW;
-    qrow = q0w + (lane & 31);
     const uint32_t rsq = (uint32_t)P.qs;
     const auto rq = FA_RSRC((const char*)P.q + hr.q0, (uint32_t)Lq * rsq);
 #pragma unroll
@@ -138,16 +125,8 @@ struct Wave8 {
     vdo0 = dma_src_v8<C>(wave, 0, lane, rsv);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) o[j] = (f32x16){};
-    b = -INFINITY;
-    lsum = 0.f;
+    this->reset_softmax();
     return true;
-  }
-
-  __device__ __forceinline__ int wave_tiles() const {
-    return q0w < Lq ? (wave_kv_end(q0w, Lq, Lk, CAUSAL) + BN - 1) / BN : 0;
-  }
-  __device__ __forceinline__ int group_tiles() const {
-    return (tile_kv_end(qt, Lq, Lk, CAUSAL, C::BM) + BN - 1) / BN;
   }
 
   __device__ __forceinline__ void dma_k(lds_char* dst, int t, int limit = 0x7fffffff) const {
@@ -209,9 +188,6 @@ struct Wave8 {
     mix<4, NDJ * NKB, 2, (4 * BN / 2) / (NDJ * NKB)>();
   }
 
-  __device__ __forceinline__ bool needs_mask(int kv0) const {
-    return (CAUSAL && kv0 + BN - 1 > q0w + off) || kv0 + BN > Lk;
-  }
   __device__ __forceinline__ void mask(f32x16 (&s)[NKB], int kv0) const {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -221,20 +197,6 @@ struct Wave8 {
         const bool vis = key < Lk && (!CAUSAL || key <= qrow + off);
         s[kb][r] = vis ? s[kb][r] : -INFINITY;
       }
-  }
-  __device__ __forceinline__ float softmax_max(const f32x16 (&s)[NKB]) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
-    mx = max_xor32(mx);
-    const float cand = vmax(b, mx * c);
-    const bool rebase = cand > b + (float)THR;
-    const float hist = rebase ? __builtin_amdgcn_exp2f(b - cand) : 1.f;
-    b = rebase ? cand : b;
-    lsum *= hist;
-    return hist;
   }
   // p = 2^(s*c - b + PSH) in (0, 256]; row sum of the unrounded p; P as
   // E4M3 bytes in key order: byte 16*(kb%2) + r of chunk kb/2 is element r
@@ -264,8 +226,8 @@ struct Wave8 {
   }
   __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NKB], u32x8 (&p)[NCH], int j) {
     const int kv0 = j * BN;
-    if (needs_mask(kv0)) mask(s, kv0);
-    const float hist = softmax_max(s);
+    if (this->needs_mask(kv0)) mask(s, kv0);
+    const float hist = this->softmax_max(s);
     rescale(j, hist);
     softmax_exp(s, p);
   }
