@@ -26,16 +26,22 @@
 // history < 1. Causal tiles wholly above the diagonal are never visited;
 // only tiles crossing the diagonal or the ragged end compare indices.
 //
-// Two kernels overlap the matrix cores and the vector ALU differently:
-//  * fa_fwd_pp (eight waves, 256 query rows): the waves form two groups
-//    whose slots alternate between an MFMA phase (P(j-1).V(j-1) and
-//    K(j).Q^T) and a softmax phase, offset by one slot, so each SIMD always
-//    holds one multiplying and one exponentiating wave; K/V use three LDS
-//    stages, issued two tiles ahead.
+// fa_fwd picks one of two kernels, which overlap the matrix cores and the
+// vector ALU differently:
+//  * fa_fwd_pp (eight waves, 256 query rows; work-group body in
+//    fa_pingpong.h): the waves form two groups whose slots alternate between
+//    an MFMA phase (P(j-1).V(j-1) and K(j).Q^T) and a softmax phase, offset
+//    by one slot, so each SIMD always holds one multiplying and one
+//    exponentiating wave; K/V use three LDS stages, issued two tiles ahead.
 //  * fa_fwd_k4 (four waves, 128 query rows), for grids too small to fill the
 //    chip with 256-row tiles: each wave overlaps the next tile's K.Q^T (and,
 //    at D=64, the previous tile's P.V) with its own current softmax; two LDS
 //    stages.
+// fa_fwd_diag can also run fa_fwd_w2 (four waves of two 32-row blocks) and
+// fa_fwd_il (eight waves, each interleaving its softmax with its next
+// tile's MFMAs; fa_interleave.h). fa_fwd_kt runs the ping-pong body on a K
+// given transposed ([D, S] per head), read like a V tile. The 8-bit kernel
+// is in fa_fwd_fp8.hip.
 //
 // Method sources: exact attention softmax(QK^T/sqrt(d)+mask)V with a
 // lower-triangle causal mask (xdnf.cn, "CUDA手写masked multi-head attention
