@@ -36,6 +36,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -57,13 +58,20 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_hbm_traffic.json")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (what changes the kernels)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash() -> str:
-    """Hash of every kernel source file (.hip and .h)."""
+    """Hash of the code (comments dropped) of every kernel source file."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
