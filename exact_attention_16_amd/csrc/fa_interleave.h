@@ -52,14 +52,11 @@ template <class W> __device__ __forceinline__ void il_body(const Problem& P) {
   typename W::STile s0, s1;  // S(j) for even j, odd j
   typename W::PTile p;
 
-  // prologue: K(0), K(1), V(0); the other stages get empty ranges (zeros),
-  // which also gives the compiler a DMA into every stage from the start
+  // prologue: K(0), K(1), V(0) (K stage 2 and V stage 1 are first written
+  // by DMA pair 0, before any read of them)
   w.dma_k(lk0, 0);
   w.dma_k(lk1, 1, ntiles);
-  w.dma_k(lk2, 2, 0);
   w.dma_v(lv0, 0);
-  w.dma_v(lv1, 1, 0);
-  w.dma_v(lv2, 2, 0);
   __builtin_amdgcn_s_waitcnt(0);
   wg_barrier();
   if (nw > 0) {

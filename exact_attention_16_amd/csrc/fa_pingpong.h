@@ -59,15 +59,11 @@ template <class W> __device__ __forceinline__ void pp_body(const Problem& P) {
     wg_barrier();
   };
 
-  // prologue: K(0), K(1), V(0) in their stages; the other stages get empty
-  // ranges so that the compiler tracks a DMA into every stage from the first
-  // block on (an LDS read then waits only for DMA into its own stage).
+  // prologue: K(0), K(1), V(0) in their stages (K stage 2 and V stages 1
+  // and 2 are first written by DMA pairs 0 and 1, before any read of them)
   w.dma_k(lk0, 0);
   w.dma_k(lk1, 1, ntiles);
-  w.dma_k(lk2, 2, 0);
   w.dma_v(lv0, 0);
-  w.dma_v(lv1, 1, 0);
-  w.dma_v(lv2, 2, 0);
   __builtin_amdgcn_s_waitcnt(0);
   wg_barrier();
 

@@ -591,14 +591,12 @@ static void check_pingpong(int ntiles, int nw, bool one_barrier) {
     issue(g, &vst[(i + 1) % NS], i + 1 < ntiles ? i + 1 : -1, slot, i);
   };
 
-  // prologue (both groups, waited with vmcnt(0) before the first barrier)
+  // prologue (both groups, waited with vmcnt(0) before the first barrier);
+  // K stage 2 and V stages 1, 2 are first written by DMA pairs 0 and 1
   for (int g = 0; g < 2; ++g) {
     issue(g, &kst[0], 0, -1, -1);
     issue(g, &kst[1], ntiles > 1 ? 1 : -1, -1, -1);
-    issue(g, &kst[2], -1, -1, -1);
     issue(g, &vst[0], 0, -1, -1);
-    issue(g, &vst[1], -1, -1, -1);
-    issue(g, &vst[2], -1, -1, -1);
     wait_all(g, -1);
   }
   auto step_reads = [&](int j, int t) {
@@ -661,7 +659,9 @@ static void check_pingpong(int ntiles, int nw, bool one_barrier) {
 // prologue reads K(0).
 static void check_il_schedule(int ntiles) {
   const int NS = kStages;
-  int ktile[3] = {0, ntiles > 1 ? 1 : -1, -1}, vtile[3] = {0, -1, -1};
+  // the prologue loads K(0), K(1), V(0); K stage 2 and V stages 1, 2 hold
+  // nothing until DMA pairs 0 and 1 (tile -2: never written)
+  int ktile[3] = {0, ntiles > 1 ? 1 : -1, -2}, vtile[3] = {0, -2, -2};
   int kpair[3] = {-1, -1, -1}, vpair[3] = {-1, -1, -1};  // pair that wrote the stage (-1: prologue)
   int kread[3] = {-1, -2, -2}, vread[3] = {-2, -2, -2};  // last iteration reading the stage
   for (int j = 0; j < ntiles; ++j) {
