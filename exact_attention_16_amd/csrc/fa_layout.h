@@ -67,17 +67,22 @@ template <int D> using CfgW2 = Cfg<D, 4, 32, 64>;
 template <int D> using CfgIL = Cfg<D, 8, 64>;
 
 // ------------------------------------------------------- work decomposition
-// One work-group per (Q tile, batch*head). Under a causal mask Q tile t needs
-// keys [0, (t+1)*BM), so work grows with t; tiles are issued heaviest first
-// (longest-processing-time order) so that the short ones fill the tail.
-// Work-group ids are dealt to the 8 XCDs round-robin (XCD = id mod 8), each
-// XCD with its own L2. When B*H is a multiple of 8, XCD x takes heads x,
-// x+8, x+16, ... one head at a time: all Q tiles of a head run together on
-// one XCD, sweeping that head's K/V through one L2. Otherwise ids go to
-// heads in turn, Q tile order outermost.
+// One work-group per (Q tile, batch*head). Work-group ids are dealt to the 8
+// XCDs round-robin (XCD = id mod 8), each XCD with its own L2.
+//  * Causal: under the mask Q tile t needs keys [0, (t+1)*BM), so work grows
+//    with t. Ids go to heads in turn with the Q tile order outermost, heaviest
+//    tiles first: longest-processing-time order over all heads, so the short
+//    tiles fill the tail. When B*H is a multiple of 8 this also keeps every
+//    head on one XCD (head h on XCD h mod 8).
+//  * Not causal: all tiles cost the same; when B*H is a multiple of 8, XCD x
+//    takes heads x, x+8, x+16, ... one head at a time, so all Q tiles of a
+//    head run together on one XCD and sweep its K/V through one L2.
+// (Measured on the long causal workload: the per-head order of the second
+// rule took 3% longer than the first; on the batched non-causal workload
+// the first took 2% longer than the second.)
 FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh) {
   int ord;
-  if ((BH & 7) == 0) {
+  if ((BH & 7) == 0 && !causal) {
     const int x = bid & 7, k = bid >> 3;  // XCD, and this id's rank on it
     const int lh = k / nqt;               // local head on the XCD
     ord = k - lh * nqt;
