@@ -149,6 +149,7 @@ struct Problem {
   float c;  // scale * log2(e) (8-bit inputs: times the Q and K descales)
   unsigned long long* events;
   float vscale;  // 8-bit inputs: the V descale, applied to O at the end
+  int hgroup;    // causal: heads an XCD takes together (block_to_tile)
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -208,7 +209,7 @@ template <class C, bool CAUSAL, int THR> struct RowState {
     hh = lane >> 5;
     c = P.c;
     int bh;
-    block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh);
+    block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh, P.hgroup);
     const int bb = bh / P.H, h = bh - bb * P.H;
     *hr = head_rows(P, bb, h);
     Lq = hr->Lq;

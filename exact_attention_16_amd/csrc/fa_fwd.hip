@@ -802,7 +802,7 @@ static int make_fixed(Problem* P, const void* q, const void* k, const void* v, v
   if (!st) return FA_ERR_NULL;
   *P = Problem{q, k, v, o, lse, st[0], st[1], st[2], st[3], st[4], st[5], st[6],
                st[7], st[8], st[9], st[10], st[11], st[12], st[13], nullptr, nullptr,
-               0, 0, B, H, Sq, Sk, 0, scale * kLog2e, nullptr};
+               0, 0, B, H, Sq, Sk, 0, scale * kLog2e, nullptr, 0.f, kHeadGroup};
   const long long nq[] = {B, H, Sq}, nk[] = {B, H, Sk > 0 ? Sk : 1};
   const long long sq_[] = {st[0], st[1], st[2]}, sk_[] = {st[3], st[4], st[5]},
                   sv_[] = {st[6], st[7], st[8]}, so_[] = {st[9], st[10], st[11]};
@@ -840,7 +840,7 @@ static int make_kt(Problem* P, const void* q, const void* k, const void* v, void
   // k's third stride is the distance between its d rows (S elements)
   *P = Problem{q, k, v, o, lse, H * hs, hs, D, H * hs, hs, S, H * hs, hs, D, H * hs, hs, D,
                (long long)H * S, S, nullptr, nullptr, 0, 0, B, H, S, S, 0, scale * kLog2e,
-               nullptr};
+               nullptr, 0.f, kHeadGroup};
   return FA_OK;
 }
 
@@ -885,7 +885,8 @@ static int make_fp8(Problem* P, const void* q, const void* k, const void* v, voi
     return FA_ERR_ALIAS;
   const long long hs = (long long)S * D;
   *P = Problem{q, k, v, o, lse, H * hs, hs, D, H * hs, hs, D, H * hs, hs, D, H * hs, hs, D,
-               (long long)H * S, S, nullptr, nullptr, 0, 0, B, H, S, S, 0, (float)c, nullptr, dv};
+               (long long)H * S, S, nullptr, nullptr, 0, 0, B, H, S, S, 0, (float)c, nullptr, dv,
+               kHeadGroup};
   return FA_OK;
 }
 
@@ -946,7 +947,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   const long long* st = strides;  // q, k, v, o as head, row; lse as head
   fa::Problem P{q, k, v, o, lse, 0, st[0], st[1], 0, st[2], st[3], 0, st[4], st[5], 0,
                 st[6], st[7], 0, st[8], cu_seqlens_q, cu_seqlens_k, total_q, total_k,
-                B, H, max_seqlen_q, max_seqlen_k, 0, scale * fa::kLog2e, nullptr};
+                B, H, max_seqlen_q, max_seqlen_k, 0, scale * fa::kLog2e, nullptr, 0.f,
+                // one sequence's heads on an XCD at a time (sequences differ in length)
+                H % 8 == 0 ? H / 8 : 1};
   const long long nq[] = {H, total_q}, nk[] = {H, total_k > 0 ? total_k : 1};
   const long long sq_[] = {st[0], st[1]}, sk_[] = {st[2], st[3]}, sv_[] = {st[4], st[5]},
                   so_[] = {st[6], st[7]};

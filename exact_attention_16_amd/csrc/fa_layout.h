@@ -68,24 +68,42 @@ template <int D> using CfgIL = Cfg<D, 8, 64>;
 
 // ------------------------------------------------------- work decomposition
 // One work-group per (Q tile, batch*head). Work-group ids are dealt to the 8
-// XCDs round-robin (XCD = id mod 8), each XCD with its own L2.
-//  * Causal: under the mask Q tile t needs keys [0, (t+1)*BM), so work grows
-//    with t. Ids go to heads in turn with the Q tile order outermost, heaviest
-//    tiles first: longest-processing-time order over all heads, so the short
-//    tiles fill the tail. When B*H is a multiple of 8 this also keeps every
-//    head on one XCD (head h on XCD h mod 8).
-//  * Not causal: all tiles cost the same; when B*H is a multiple of 8, XCD x
-//    takes heads x, x+8, x+16, ... one head at a time, so all Q tiles of a
-//    head run together on one XCD and sweep its K/V through one L2.
-// (Measured on the long causal workload: the per-head order of the second
-// rule took 3% longer than the first; on the batched non-causal workload
-// the first took 2% longer than the second.)
-FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh) {
+// XCDs round-robin (XCD = id mod 8), each XCD with its own L2. When B*H is a
+// multiple of 8, XCD x takes heads x, x+8, x+16, ... (local heads 0, 1, ...),
+// so every head's K/V stays in one L2:
+//  * Not causal: all tiles cost the same; the XCD takes its heads one at a
+//    time, all Q tiles of a head together.
+//  * Causal: Q tile t needs keys [0, (t+1)*BM), so work grows with t. The
+//    XCD takes its heads in groups of hg, and within a group the Q tiles in
+//    turn over the group's heads, heaviest first (longest-processing-time
+//    order), so the short tiles fill the tail. The launcher picks hg:
+//    kHeadGroup for sequences of one length, and for a variable-length
+//    batch the heads one sequence puts on an XCD, so that sequences of
+//    different lengths are not mixed. (Measured on the long causal
+//    workload, 4 heads per XCD: groups of 1 took 3% longer than 4. On the
+//    variable-length batch, 32 heads per XCD: groups of 4 took 12% and of
+//    32 took 15% longer than groups of 2, one sequence.)
+// Otherwise ids go to heads in turn, Q tile order outermost (heaviest first
+// when causal).
+constexpr int kHeadGroup = 4;
+FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh,
+                         int hg = kHeadGroup) {
   int ord;
-  if ((BH & 7) == 0 && !causal) {
+  if ((BH & 7) == 0) {
     const int x = bid & 7, k = bid >> 3;  // XCD, and this id's rank on it
-    const int lh = k / nqt;               // local head on the XCD
-    ord = k - lh * nqt;
+    int lh;                               // local head on the XCD
+    if (!causal) {
+      lh = k / nqt;
+      ord = k - lh * nqt;
+    } else {
+      const int hx = BH >> 3;                  // heads on this XCD
+      const int g = k / (hg * nqt);            // head group
+      const int h0 = g * hg;
+      const int gn = hx - h0 < hg ? hx - h0 : hg;  // heads in it
+      const int r = k - h0 * nqt;              // rank within the group
+      ord = r / gn;
+      lh = h0 + (r - ord * gn);
+    }
     *bh = x + 8 * lh;
   } else {
     ord = bid / BH;

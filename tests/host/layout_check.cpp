@@ -519,6 +519,34 @@ static void check_global8(int B, int H, int Sq, int Sk, bool causal, uint32_t rs
     for (size_t p = 0; p < owritten.size(); ++p) CHECK(owritten[p], "O8 element not written");
 }
 
+// The work-group map for every head-group size a launch can pick: a
+// bijection of ids onto (Q tile, head), every head on XCD head mod 8 when
+// B*H is a multiple of 8, and causal tiles of a group in descending order.
+static void check_tile_map() {
+  const int bhs[] = {1, 3, 8, 16, 24, 64, 256, 640}, nqts[] = {1, 3, 32};
+  const int hgs[] = {1, 2, 3, 4, 8};
+  for (int BH : bhs)
+    for (int nqt : nqts)
+      for (int hg : hgs)
+        for (int causal = 0; causal < 2; ++causal) {
+          std::vector<char> seen((size_t)BH * nqt, 0);
+          std::vector<int> last_qt(BH, 1 << 30);
+          for (int bid = 0; bid < BH * nqt; ++bid) {
+            int qt, bh;
+            block_to_tile(bid, BH, nqt, causal != 0, &qt, &bh, hg);
+            CHECK(qt >= 0 && qt < nqt && bh >= 0 && bh < BH, "tile map range");
+            if (!(qt >= 0 && qt < nqt && bh >= 0 && bh < BH)) continue;
+            CHECK(!seen[(size_t)qt * BH + bh], "tile map not one-to-one BH=%d nqt=%d hg=%d", BH, nqt, hg);
+            seen[(size_t)qt * BH + bh] = 1;
+            if (BH % 8 == 0) CHECK(bh % 8 == bid % 8, "head off its XCD");
+            if (causal) {  // each head's tiles come heaviest first
+              CHECK(qt < last_qt[bh], "causal tiles of a head out of order");
+              last_qt[bh] = qt;
+            }
+          }
+        }
+}
+
 // ------------------------------------------------ ping-pong schedule replay
 // One DMA share (one wave's issues) of a tile into a stage.
 struct Share {
@@ -722,6 +750,8 @@ int main() {
   check_lds<Cfg8<128>>();
   check_lds<CfgW2<64>>();
   check_lds<CfgW2<128>>();
+  check_tile_map();
+  std::printf("work-group map: every head-group size: checked\n");
   for (int ntiles = 1; ntiles <= 40; ++ntiles) check_w2_schedule(ntiles);
   std::printf("two-block schedule: ntiles 1..40: checked\n");
   for (int ntiles = 1; ntiles <= 12; ++ntiles)
