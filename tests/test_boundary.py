@@ -303,3 +303,20 @@ def test_kt_validation_rejects(kw, expect):
 def test_kt_empty_problem_is_a_noop():
     assert _call_kt(S=0) == OK
     assert _call_kt(B=0, q=0, k=0, v=0, o=0, lse=0) == OK
+
+
+# ------------------------------------------------ torch helpers, host side
+def test_torch_helpers_reject_host_tensors_before_any_launch():
+    import torch
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q, True)
+    with pytest.raises(ValueError):
+        fa.attention_kt(q, q.transpose(-1, -2).contiguous(), q, True)
+    q8 = torch.zeros((1, 1, 8, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        fa.attention_fp8(q8, q8, q8, 1.0, 1.0, 1.0, True)
+    with pytest.raises(ValueError):
+        fa.attention_varlen(q[0, 0][:, None, :], q[0, 0][:, None, :], q[0, 0][:, None, :],
+                            torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                            8, 8, True)
