@@ -126,6 +126,21 @@ def test_long_context_max_rows():
     assert eo <= O_TOL[dt] and el <= LSE_TOL
 
 
+def test_two_million_rows():
+    """One head at S = 2^21 (a head's K, V and O span 2^29 bytes, a quarter of
+    the 32-bit offset range), causal bf16, sampled rows near both ends."""
+    S, dt = 1 << 21, W.BF16
+    _banner(f"S={S}")
+    qb, kb, vb = (W.random_bits((1, 1, S, 128), dt, 88 + i) for i in range(3))
+    o, lse = run(qb, kb, vb, dt, True, 128 ** -0.5)
+    og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(lg).all()
+    rows = np.array([0, 1, 255, 256, S // 2 + 7, S - 257, S - 256, S - 2, S - 1])
+    eo, el = compare_rows(qb, kb, vb, dt, True, 128 ** -0.5, og, lg, [((0, 0), rows)])
+    _banner(f"S={S}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= O_TOL[dt] and el <= LSE_TOL
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
