@@ -320,3 +320,26 @@ def test_torch_helpers_reject_host_tensors_before_any_launch():
         fa.attention_varlen(q[0, 0][:, None, :], q[0, 0][:, None, :], q[0, 0][:, None, :],
                             torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                             8, 8, True)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    """No library, no fallback: loading raises and names the build step."""
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.fa_version()
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The package and the benchmark's timed path never touch oracle/."""
+    pkg = os.path.join(ROOT, "exact_attention_16_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            text = open(os.path.join(pkg, name)).read()
+            assert "oracle" not in text, name
+    bench = open(os.path.join(ROOT, "bench.py")).read()
+    # the only use: the cpu_baseline leg, imported inside that function
+    assert bench.count("import oracle") == 1
+    assert "def cpu_baseline" in bench.split("import oracle")[0].rsplit("\n\n\n", 1)[-1]
