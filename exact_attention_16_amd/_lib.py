@@ -26,6 +26,7 @@ VARIANT_FOUR_WAVE = 1
 VARIANT_PING_PONG = 2
 VARIANT_TWO_BLOCK = 3
 VARIANT_INTERLEAVE = 4
+VARIANT_PERSISTENT = 5
 
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_DIM", -3: "FA_ERR_UNSUPPORTED",

@@ -202,14 +202,16 @@ template <class C, bool CAUSAL, int THR> struct RowState {
   // rows) and its sequence; false when the work-group's query tile lies
   // wholly past the sequence's end (the same for every wave of the
   // work-group, which then returns before any DMA or barrier).
-  __device__ __forceinline__ bool locate(const Problem& P, int sub, HeadRows* hr) {
+  // id: the work item (Q tile, head) in launch order; the work-group's
+  // own id unless a persistent work-group passes the one it is on.
+  __device__ __forceinline__ bool locate(const Problem& P, int sub, HeadRows* hr, int id) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hh = lane >> 5;
     c = P.c;
     int bh;
-    block_to_tile(blockIdx.x, P.B * P.H, P.nqt, CAUSAL, &qt, &bh, P.hgroup);
+    block_to_tile(id, P.B * P.H, P.nqt, CAUSAL, &qt, &bh, P.hgroup);
     const int bb = bh / P.H, h = bh - bb * P.H;
     *hr = head_rows(P, bb, h);
     Lq = hr->Lq;

@@ -136,9 +136,9 @@ struct Wave : RowState<C, CAUSAL, THR> {
   // Sets up this wave's rows of the work-group's query tile (see
   // RowState::locate); false when the tile lies wholly past its sequence's
   // end. sub: which 32-row block of the wave's C::RPW rows this object holds
-  __device__ __forceinline__ bool init(const Problem& P, int sub = 0) {
+  __device__ __forceinline__ bool init(const Problem& P, int sub = 0, int id = -1) {
     HeadRows hr;
-    if (!this->locate(P, sub, &hr)) return false;
+    if (!this->locate(P, sub, &hr, id < 0 ? (int)blockIdx.x : id)) return false;
     const long long q0 = hr.q0, k0 = hr.k0, v0 = hr.v0, o0 = hr.o0, l0 = hr.l0;
     Kh = (const char*)P.k + k0 * 2;
     Vh = (const char*)P.v + v0 * 2;
@@ -329,6 +329,14 @@ __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_pp(const Problem P) {
   pp_body<Wave<T, Cfg8<D>, CAUSAL, THR, DIAG>>(P);
+}
+
+// ------------------------------------------------- persistent ping-pong
+template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_pp_persist(const Problem P) {
+  pp_persistent<Wave<T, Cfg8<D>, CAUSAL, THR, DIAG>>(P);
 }
 
 // ------------------------------------------------- K given transposed
@@ -643,7 +651,18 @@ fa_fwd_k4(const Problem P) {
 // one work-group per compute unit, else the four-wave kernel.
 constexpr long long kPingPongMinGroups = 256;
 
-enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kTwoBlock = 3, kInterleave = 4 };
+enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kTwoBlock = 3, kInterleave = 4,
+               kPersistent = 5 };
+
+// Work-groups of the persistent kernel: one per CU of the current device,
+// rounded down to a multiple of the 8 XCDs.
+static int persistent_groups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus / 8 * 8;
+}
 
 template <int D> static bool use_pingpong(int BH, int S, int variant) {
   if (variant == kFourWave) return false;
@@ -654,7 +673,13 @@ template <int D> static bool use_pingpong(int BH, int S, int variant) {
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 static int launch_one(Problem P, hipStream_t stream, int variant) {
   const int BH = P.B * P.H;
-  if (variant == kInterleave) {
+  if (variant == kPersistent) {
+    P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);
+    const int g = persistent_groups();
+    if (g <= 0) return FA_ERR_HIP;
+    hipLaunchKernelGGL((fa_fwd_pp_persist<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)g),
+                       dim3(Cfg8<D>::threads), 0, stream, P);
+  } else if (variant == kInterleave) {
     P.nqt = num_q_tiles(P.Sq, CfgIL<D>::BM);
     hipLaunchKernelGGL((fa_fwd_il<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
                        dim3(CfgIL<D>::threads), 0, stream, P);
@@ -969,7 +994,7 @@ int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse
   const int r = fa::make_fixed(&P, q, k, v, o, lse, B, H, S, S, D, causal, scale, dtype, st, &empty);
   if (r != FA_OK) return r;
   if (threshold_log2 != 0 && threshold_log2 != 8) return FA_ERR_ARG;
-  if (variant < fa::kAuto || variant > fa::kInterleave) return FA_ERR_ARG;
+  if (variant < fa::kAuto || variant > fa::kPersistent) return FA_ERR_ARG;
   if (!rescale_events) return FA_ERR_NULL;
   if (((uintptr_t)rescale_events & 7) != 0) return FA_ERR_ALIGN;
   if (empty) return FA_OK;

@@ -97,9 +97,9 @@ struct Wave8 : RowState<C_, CAUSAL, THR> {
   u32x8 qf[NDJ];
   f32x16 o[NDB];
 
-  __device__ __forceinline__ bool init(const Problem& P) {
+  __device__ __forceinline__ bool init(const Problem& P, int id = -1) {
     HeadRows hr;
-    if (!this->locate(P, 0, &hr)) return false;
+    if (!this->locate(P, 0, &hr, id < 0 ? (int)blockIdx.x : id)) return false;
     vscale = P.vscale;
     // one-byte Q, K, V elements; two-byte O elements
     Kh = (const char*)P.k + hr.k0;

@@ -114,6 +114,15 @@ FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh
 
 FA_HD int num_q_tiles(int S, int BM) { return (S + BM - 1) / BM; }
 
+// Work item of a persistent work-group b (of G, a multiple of 8) at round k:
+// a snake over the ranks of its XCD (see pp_persistent); -1 past the last.
+FA_HD int persistent_item(int b, int G, int k, int total) {
+  const int x = b & 7, c = b >> 3, cg = G >> 3;
+  const int r = k * cg + ((k & 1) ? cg - 1 - c : c);
+  const long long id = 8LL * r + x;
+  return id < total ? (int)id : -1;
+}
+
 // Causal masks are aligned bottom-right: with Lq queries and Lk keys, query i
 // sees keys j <= i + (Lk - Lq). With Lq == Lk that is j <= i.
 FA_HD int clamp_keys(int e, int Lk) { return e < 0 ? 0 : (e < Lk ? e : Lk); }

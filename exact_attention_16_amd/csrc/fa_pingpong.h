@@ -10,11 +10,30 @@
 
 namespace fa {
 
+template <class W>
+__device__ __forceinline__ void pp_item(const Problem& P, W& w, lds_char* const lk0,
+                                        lds_char* const lk1, lds_char* const lk2,
+                                        lds_char* const lv0, lds_char* const lv1,
+                                        lds_char* const lv2);
+
+// The stage arrays of the ping-pong work-group, declared by each body.
+#define FA_PP_STAGES(TB)                                              \
+  __shared__ __attribute__((aligned(1024))) char a_vstage0[TB];      \
+  __shared__ __attribute__((aligned(1024))) char a_vstage1[TB];      \
+  __shared__ __attribute__((aligned(1024))) char a_vstage2[TB];      \
+  __shared__ __attribute__((aligned(1024))) char b_kstage0[TB];      \
+  __shared__ __attribute__((aligned(1024))) char b_kstage1[TB];      \
+  __shared__ __attribute__((aligned(1024))) char b_kstage2[TB];      \
+  lds_char* const lk0 = (lds_char*)b_kstage0;                        \
+  lds_char* const lk1 = (lds_char*)b_kstage1;                        \
+  lds_char* const lk2 = (lds_char*)b_kstage2;                        \
+  lds_char* const lv0 = (lds_char*)a_vstage0;                        \
+  lds_char* const lv1 = (lds_char*)a_vstage1;                        \
+  lds_char* const lv2 = (lds_char*)a_vstage2;
+
 template <class W> __device__ __forceinline__ void pp_body(const Problem& P) {
   using C = typename W::Config;
   constexpr int TB = C::tileBytes;
-  constexpr int DPW = C::dmaPerWave;
-  constexpr bool ONE = pp_one_barrier<W::D>;  // one barrier per step, else two
   static_assert(kStages == 3, "the step below is unrolled over three stages");
   // One array per stage: with the stage fixed at compile time the compiler
   // sees that an LDS read never aliases the DMA in flight into another stage
@@ -23,21 +42,50 @@ template <class W> __device__ __forceinline__ void pp_body(const Problem& P) {
   // reads (two per P.V MFMA, the part of the MFMA phase with the most
   // instructions per MFMA) mostly fit the 16-bit offset field of the LDS
   // instruction and need no address arithmetic. This affects speed only.
-  __shared__ __attribute__((aligned(1024))) char a_vstage0[TB];
-  __shared__ __attribute__((aligned(1024))) char a_vstage1[TB];
-  __shared__ __attribute__((aligned(1024))) char a_vstage2[TB];
-  __shared__ __attribute__((aligned(1024))) char b_kstage0[TB];
-  __shared__ __attribute__((aligned(1024))) char b_kstage1[TB];
-  __shared__ __attribute__((aligned(1024))) char b_kstage2[TB];
-  lds_char* const lk0 = (lds_char*)b_kstage0;
-  lds_char* const lk1 = (lds_char*)b_kstage1;
-  lds_char* const lk2 = (lds_char*)b_kstage2;
-  lds_char* const lv0 = (lds_char*)a_vstage0;
-  lds_char* const lv1 = (lds_char*)a_vstage1;
-  lds_char* const lv2 = (lds_char*)a_vstage2;
+  FA_PP_STAGES(TB)
 
   W w;
   if (!w.init(P)) return;
+  pp_item(P, w, lk0, lk1, lk2, lv0, lv1, lv2);
+}
+
+// The persistent form: a fixed grid (a multiple of 8 work-groups, one per
+// CU) in which each work-group runs work items one after another, without
+// a new launch per item. Work-group b on XCD x = b mod 8 (index c = b / 8
+// among the G/8 work-groups of its XCD) takes, at round k, the item of rank
+// k*G/8 + c on its XCD for even k and k*G/8 + G/8 - 1 - c for odd k: ranks
+// follow the launch order of block_to_tile (heaviest first when causal), so
+// the snake pairs heavy items with light ones. Its item ids rise with k,
+// so the first id past the end ends the work-group.
+template <class W> __device__ __forceinline__ void pp_persistent(const Problem& P) {
+  using C = typename W::Config;
+  constexpr int TB = C::tileBytes;
+  FA_PP_STAGES(TB)
+
+  const int total = P.nqt * P.B * P.H;
+  for (int k = 0;; ++k) {
+    const int id = persistent_item(blockIdx.x, gridDim.x, k, total);
+    if (id < 0) break;
+    // value-initialised: every member is defined at the top of the item, so
+    // no register of the previous item is carried around the loop (left
+    // undefined, they were, and the D = 128 body then spilled)
+    W w{};
+    if (!w.init(P, 0, id)) continue;  // the same for every wave
+    pp_item(P, w, lk0, lk1, lk2, lv0, lv1, lv2);
+    wg_barrier();  // the next item's prologue refills the stages
+  }
+}
+
+// One work item (Q tile, head) of the ping-pong work-group, after w.init:
+// prologue DMA, the slots of both wave groups, and the epilogue.
+template <class W>
+__device__ __forceinline__ void pp_item(const Problem& P, W& w, lds_char* const lk0,
+                                        lds_char* const lk1, lds_char* const lk2,
+                                        lds_char* const lv0, lds_char* const lv1,
+                                        lds_char* const lv2) {
+  using C = typename W::Config;
+  constexpr int DPW = C::dmaPerWave;
+  constexpr bool ONE = pp_one_barrier<W::D>;  // one barrier per step, else two
   const int grp = w.wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   const int ntiles = w.group_tiles();
   const int nw = w.wave_tiles();

@@ -179,12 +179,16 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *                    per wave (256 rows, 32-key tiles), 4 = the eight-wave
  *                    kernel in which every wave overlaps its own softmax
  *                    with its next tile's MFMAs (256 rows, 64-key tiles;
- *                    the "interleaved" kernel). Every variant
- *                    computes the same result, to rounding; the choice only
- *                    affects speed.
+ *                    the "interleaved" kernel), 5 = the eight-wave
+ *                    ping-pong kernel in persistent form (one work-group
+ *                    per CU of the current device, rounded down to a
+ *                    multiple of 8, each running query tiles in turn).
+ *                    Every variant computes the same result, to rounding;
+ *                    the choice only affects speed.
  * It runs separate, instrumented instantiations of the same kernels.
  * Invalid threshold_log2 or variant: FA_ERR_ARG; NULL rescale_events:
- * FA_ERR_NULL; rescale_events not 8-byte aligned: FA_ERR_ALIGN.
+ * FA_ERR_NULL; rescale_events not 8-byte aligned: FA_ERR_ALIGN; the CU
+ * count of the current device not readable (variant 5): FA_ERR_HIP.
  */
 int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int S, int D, int causal, float scale,

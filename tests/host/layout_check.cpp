@@ -752,6 +752,32 @@ int main() {
   check_lds<CfgW2<128>>();
   check_tile_map();
   std::printf("work-group map: every head-group size: checked\n");
+  // persistent work-groups: every item exactly once, ids rising per group
+  for (int G : {8, 16, 256, 264})
+    for (int total : {1, 7, 8, 100, 256, 1000, 1024, 8192}) {
+      std::vector<int> cnt(total, 0);
+      for (int b = 0; b < G; ++b) {
+        int last = -1;
+        for (int k = 0;; ++k) {
+          const int id = persistent_item(b, G, k, total);
+          if (id < 0) break;
+          CHECK(id > last && id % 8 == b % 8, "persistent ids must rise and stay on the XCD");
+          last = id;
+          ++cnt[id];
+        }
+        // nothing valid comes after the first id past the end
+        for (int k = 0; k < 4 * (total / G + 2); ++k) {
+          const int r = k * (G / 8) + ((k & 1) ? G / 8 - 1 - b / 8 : b / 8);
+          if (8LL * r + b % 8 >= total) {
+            for (int k2 = k + 1; k2 < k + 4; ++k2)
+              CHECK(persistent_item(b, G, k2, total) < 0, "persistent item after the end");
+            break;
+          }
+        }
+      }
+      for (int id = 0; id < total; ++id) CHECK(cnt[id] == 1, "persistent item %d run %d times", id, cnt[id]);
+    }
+  std::printf("persistent work-group order: checked\n");
   for (int ntiles = 1; ntiles <= 40; ++ntiles) check_w2_schedule(ntiles);
   std::printf("two-block schedule: ntiles 1..40: checked\n");
   for (int ntiles = 1; ntiles <= 12; ++ntiles)

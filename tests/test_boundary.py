@@ -48,10 +48,10 @@ def test_kernel_launch_stubs_are_defined():
         pytest.skip("no nm")
     out = subprocess.run([nm, "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
     stubs = [l for l in out.splitlines() if "device_stub" in l]
-    # 4 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic
+    # 5 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic
     # thresholds), the transposed-K kernel x 2 dtypes x 2 head dims x 2 masks,
     # and the 8-bit kernel x 2 head dims x 2 masks
-    assert len(stubs) == 108
+    assert len(stubs) == 132
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
@@ -127,12 +127,12 @@ def test_diag_validation():
     args = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 8, 64, 0, 0.1, None, 0)
     ev = 0x20000000000
     assert fa.fa_fwd_diag(*args, 3, 0, ev, check=False) == ARG
-    assert fa.fa_fwd_diag(*args, 8, 5, ev, check=False) == ARG
+    assert fa.fa_fwd_diag(*args, 8, 6, ev, check=False) == ARG
     assert fa.fa_fwd_diag(*args, 8, -1, ev, check=False) == ARG
     assert fa.fa_fwd_diag(*args, 8, 0, 0, check=False) == NULL
     assert fa.fa_fwd_diag(*args, 0, 2, ev + 4, check=False) == ALIGN
     e = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 0, 64, 0, 0.1, None, 0)
-    for variant in (0, 1, 2, 3, 4):
+    for variant in (0, 1, 2, 3, 4, 5):
         assert fa.fa_fwd_diag(*e, 8, variant, ev, check=False) == OK
 
 

@@ -24,7 +24,7 @@ def _banner(msg):
 
 
 VARIANTS = {"k4": fa.VARIANT_FOUR_WAVE, "pp": fa.VARIANT_PING_PONG, "w2": fa.VARIANT_TWO_BLOCK,
-            "il": fa.VARIANT_INTERLEAVE}
+            "il": fa.VARIANT_INTERLEAVE, "ps": fa.VARIANT_PERSISTENT}
 
 
 def _check_full(qb, kb, vb, dtype, causal, scale, tag, variant=None):
@@ -47,7 +47,7 @@ def test_tiny_workload(causal):
     _check_full(*W.make_inputs(w), w.dtype, causal, w.scale, f"tiny causal={causal}")
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
@@ -62,7 +62,7 @@ def test_small_shapes_all_rows(S, causal, D, dtype, kernel):
                 f"S={S} D={D} {dtype} causal={causal} kernel={kernel}", VARIANTS[kernel])
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_many_tiles_all_rows(causal, D, kernel):
@@ -82,7 +82,7 @@ def test_kernels_agree(D):
     S, dt = 777, W.F16
     qb, kb, vb = (W.random_bits((2, 2, S, D), dt, 3000 + D + i) for i in range(3))
     res = [_check_full(qb, kb, vb, dt, True, D ** -0.5, f"agree D={D} {k}", VARIANTS[k])
-           for k in ("k4", "pp", "w2", "il")]
+           for k in ("k4", "pp", "w2", "il", "ps")]
     for other in res[1:]:
         assert np.abs(res[0][0] - other[0]).max() <= O_TOL[dt]
         assert np.abs(res[0][1] - other[1]).max() <= LSE_TOL
@@ -222,7 +222,7 @@ def _diag(qb, kb, vb, dtype, causal, scale, thr, variant=0):
     return o_to_f64(o), lse.cpu().numpy().astype(np.float64), int(ev.item())
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_lagging_and_eager_rescale_both_match(D, kernel):
     """Threshold 8 (production) and 0 (eager) both meet tolerance on a steep
@@ -249,7 +249,8 @@ def test_lagging_and_eager_rescale_both_match(D, kernel):
     # the float64 model of the algorithm, same KV tile size
     # KV tile of the forced kernel: the eight-wave kernel's from the tile
     # query on a grid large enough for fa_fwd to pick it
-    bn = {"k4": 64, "pp": fa.fa_fwd_tile(D, 1, 256, 1024)[1], "w2": 32, "il": 64}[kernel]
+    bn = {"k4": 64, "pp": fa.fa_fwd_tile(D, 1, 256, 1024)[1], "w2": 32, "il": 64,
+          "ps": fa.fa_fwd_tile(D, 1, 256, 1024)[1]}[kernel]
     model = {8: 0, 0: 0}
     for h in range(w.H):
         q, k, v = (W.decode(x[0, h], dt) for x in (qb, kb, vb))
@@ -272,7 +273,7 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il"])
+@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_no_writes_outside_outputs(D, kernel):
     """Outputs embedded in guard bands: the kernel writes only O and lse."""
