@@ -60,6 +60,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
 #define FA_RSRC(base, bytes) \
   __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>((const void*)(base)), 0, (int)(bytes), kBufferWord3)
 
+// Byte count of a DMA source range: `bytes` when `live`, else 0 (an empty
+// range, which the DMA turns into zeros). A product rather than a select:
+// the compiler turns the select of a uniform condition into branches that
+// split the DMA issue into blocks of its own. The 8-bit kernel runs about 1%
+// faster this way; the 16-bit kernels' time is unchanged.
+__device__ __forceinline__ uint32_t dma_bytes(bool live, uint32_t bytes) {
+  return bytes * (uint32_t)live;
+}
+
 // LDS pointers stay in address space 3 from the point where each shared
 // array is declared (a cast of a generic pointer to address space 3 would
 // make the host compilation pass drop the kernel launch stubs).

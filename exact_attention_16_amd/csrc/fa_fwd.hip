@@ -175,7 +175,7 @@ struct Wave : RowState<C, CAUSAL, THR> {
       // D rows of keys kv0 .. kv0+BN-1; the range runs to the end of this
       // head's [D, S] block. Keys past Lk read the next row's values (or
       // zeros past the block): finite, and masked like any key past the end.
-      const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)D * rsk - (uint32_t)kv0 * 2u : 0u;
+      const uint32_t bytes = dma_bytes((t < limit) & (kv0 < Lk), (uint32_t)D * rsk - (uint32_t)kv0 * 2u);
       const auto r = FA_RSRC(Kh + (size_t)kv0 * 2, bytes);
 #pragma unroll
       for (int i = 0; i < DPW; ++i) {
@@ -183,7 +183,7 @@ struct Wave : RowState<C, CAUSAL, THR> {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lp, 16, kdo0 + i * dsk, 0, 0, 0);
       }
     } else {
-      const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsk : 0u;
+      const uint32_t bytes = dma_bytes((t < limit) & (kv0 < Lk), (uint32_t)(Lk - kv0) * rsk);
       const auto r = FA_RSRC(Kh + (size_t)kv0 * rsk, bytes);
 #pragma unroll
       for (int i = 0; i < DPW; ++i) {
@@ -196,7 +196,7 @@ struct Wave : RowState<C, CAUSAL, THR> {
   }
   __device__ __forceinline__ void dma_v(lds_char* dst, int t, int limit = 0x7fffffff) const {
     const int kv0 = t * BN;
-    const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsv : 0u;
+    const uint32_t bytes = dma_bytes((t < limit) & (kv0 < Lk), (uint32_t)(Lk - kv0) * rsv);
     const auto r = FA_RSRC(Vh + (size_t)kv0 * rsv, bytes);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {

@@ -131,7 +131,7 @@ struct Wave8 : RowState<C_, CAUSAL, THR> {
 
   __device__ __forceinline__ void dma_k(lds_char* dst, int t, int limit = 0x7fffffff) const {
     const int kv0 = t * BN;
-    const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsk : 0u;
+    const uint32_t bytes = dma_bytes((t < limit) & (kv0 < Lk), (uint32_t)(Lk - kv0) * rsk);
     const auto r = FA_RSRC(Kh + (size_t)kv0 * rsk, bytes);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
@@ -141,7 +141,7 @@ struct Wave8 : RowState<C_, CAUSAL, THR> {
   }
   __device__ __forceinline__ void dma_v(lds_char* dst, int t, int limit = 0x7fffffff) const {
     const int kv0 = t * BN;
-    const uint32_t bytes = t < limit && kv0 < Lk ? (uint32_t)(Lk - kv0) * rsv : 0u;
+    const uint32_t bytes = dma_bytes((t < limit) & (kv0 < Lk), (uint32_t)(Lk - kv0) * rsv);
     const auto r = FA_RSRC(Vh + (size_t)kv0 * rsv, bytes);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
