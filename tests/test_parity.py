@@ -222,6 +222,19 @@ def _diag(qb, kb, vb, dtype, causal, scale, thr, variant=0):
     return o_to_f64(o), lse.cpu().numpy().astype(np.float64), int(ev.item())
 
 
+@pytest.mark.parametrize("name", ["long", "bat"])
+def test_persistent_equals_pingpong_full_size(name):
+    """The persistent form runs the ping-pong kernel's per-item code with the
+    work items in another order, so at the full workload sizes its output is the
+    ping-pong kernel's bit for bit."""
+    w = W.WORKLOADS[name]
+    _banner(f"persistent vs ping-pong, {name}: B={w.B} H={w.H} S={w.S} D={w.D}")
+    qb, kb, vb = W.make_inputs(w)
+    o2, l2, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, fa.VARIANT_PING_PONG)
+    o5, l5, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, fa.VARIANT_PERSISTENT)
+    assert np.array_equal(o2, o5) and np.array_equal(l2, l5)
+
+
 @pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_lagging_and_eager_rescale_both_match(D, kernel):
