@@ -325,6 +325,43 @@ def test_side_stream_and_typed_wrappers():
     assert torch.equal(o2, ref_o) and torch.equal(l2, ref_l)
 
 
+def test_concurrent_host_threads():
+    """The library keeps no mutable state: two host threads calling it at once,
+    each on its own stream with its own shapes, get exactly the results of
+    single-threaded calls."""
+    import threading
+    cases = [((1, 4, 700, 128), W.BF16, True, 70), ((2, 3, 513, 64), W.F16, False, 80)]
+    refs, inputs = [], []
+    for shape, dt, causal, seed in cases:
+        bits = tuple(W.random_bits(shape, dt, seed + i) for i in range(3))
+        inputs.append(tuple(to_dev(x, dt) for x in bits))
+        refs.append(run(*bits, dt, causal, shape[3] ** -0.5))
+    torch.cuda.synchronize()  # the threads' streams do not wait for these copies
+    errors = []
+
+    def worker(n):
+        (q, k, v), (_, _, causal, _) = inputs[n], cases[n]
+        s = torch.cuda.Stream()  # default priority
+        try:
+            for _ in range(25):
+                with torch.cuda.stream(s):
+                    o, l = fa.attention(q, k, v, causal, stream=s)
+                s.synchronize()
+                if not (torch.equal(o, refs[n][0]) and torch.equal(l, refs[n][1])):
+                    errors.append(f"thread {n}: result differs")
+                    return
+        except Exception as e:  # reported below, in the main thread
+            errors.append(f"thread {n}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+
+
 def test_empty_inputs_launch_nothing():
     z = torch.empty((0,), dtype=torch.float16, device=device())
     assert fa.fa_fwd(z.data_ptr(), z.data_ptr(), z.data_ptr(), z.data_ptr(), 0, 1, 4, 0, 64, 1,
