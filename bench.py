@@ -89,6 +89,105 @@ def load_traffic(workload: str):
 
 
 CALIBRATION_BYTES = 1 << 30  # each --calibrate-copy copy reads and writes 1 GiB
+PEAK_SCLK_MHZ = 2400.0  # engine clock at which the published peaks are quoted
+
+
+class ClockSampler:
+    """Samples the GPU engine clock (MHz) in a background thread while a
+    timed region runs: the current level of sysfs pp_dpm_sclk, else amdsmi's
+    GPU metrics (the mean of the per-XCD gfx clocks, with socket power).
+    The published peaks assume 2.4 GHz; under sustained MFMA load the part
+    holds a lower clock, which this records beside every timing."""
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+        self.period = period_s
+        self.samples: list[float] = []
+        self.power: list[float] = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = self._setup()
+
+    def _setup(self):
+        # sysfs first: its current level is re-read on every access, while
+        # amdsmi's metrics table refreshes too slowly for a sub-second region
+        import glob
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            def read_sysfs(path=path):
+                with open(path) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            return float(re.findall(r"(\d+)\s*[Mm]hz", line)[0]), None
+                return None, None
+            try:
+                if read_sysfs()[0] is not None:
+                    self.source = f"sysfs {path}"
+                    return read_sysfs
+            except Exception:
+                continue
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read_smi():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clks = m.get("current_gfxclks")
+                vals = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 10000] \
+                    if isinstance(clks, list) else []
+                p = m.get("current_socket_power")
+                return (sum(vals) / len(vals) if vals else None,
+                        float(p) if isinstance(p, (int, float)) and 0 < p < 5000 else None)
+
+            if read_smi()[0] is not None:
+                self.source = "amdsmi gpu_metrics current_gfxclks"
+                return read_smi
+        except Exception:
+            pass
+        return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                c, p = self._read()
+            except Exception:
+                return
+            if c is not None:
+                self.samples.append(c)
+            if p is not None:
+                self.power.append(p)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._read is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=5)
+        return False
+
+    def report(self) -> dict:
+        """Mean / min / max engine clock over the samples, with the source."""
+        if not self.samples:
+            return {"sclk_mhz": None, "source": self.source, "samples": 0}
+        s = self.samples
+        return {"sclk_mhz": sum(s) / len(s), "sclk_min_mhz": min(s), "sclk_max_mhz": max(s),
+                "samples": len(s), "source": self.source,
+                "socket_power_w": sum(self.power) / len(self.power) if self.power else None}
+
+
+def clock_fields(tflops: float, peak: float, clk: dict) -> dict:
+    """The bench line's clock entries: the sampled clock and the fraction of
+    the peak re-derived at that clock (peak x sclk / 2400 MHz)."""
+    mhz = clk.get("sclk_mhz")
+    return {"sclk": clk,
+            "pct_of_peak_at_sclk": 100 * tflops / (peak * mhz / PEAK_SCLK_MHZ) if mhz else None}
 
 
 def kernel_name(w) -> str:
@@ -207,6 +306,12 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="long", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", dest="cold", action="store_true", default=None,
+                    help="also time launches one by one after a cache scrub (default: only "
+                         "for workloads under 64 MiB)")
+    ap.add_argument("--no-cold", dest="cold", action="store_false")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of plain device fills before the warm-up steps (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run plain 1 GiB device copies first (counter scaling)")
     ap.add_argument("--varlen", action="store_true",
@@ -249,38 +354,15 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     if args.calibrate_copy:
         calibrate_copy(torch, dev, stream)
+    settled = settle(torch, dev, stream, args.settle_s)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: K back-to-back launches on `stream`, events on that stream
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
+    ms_per_step, wall, med_ms, clk = timed(step, stream, torch, args.steps, args.warmup)
+    gpu_ms = ms_per_step * args.steps
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     assert bool(torch.isfinite(lse).all()), "non-finite output"
-
-    # per-launch durations (events around each launch), median
-    per = []
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * min(args.steps, 20))]
-    for i in range(0, len(evs), 2):
-        evs[i].record(stream)
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    for i in range(0, len(evs), 2):
-        per.append(evs[i].elapsed_time(evs[i + 1]))
-    med_ms = float(np.median(per))
+    cold = None
+    if args.cold or (args.cold is None and w.algorithmic_bytes < COLD_MAX_BYTES):
+        cold = cold_timing(step, stream, torch, dev, w.algorithmic_bytes)
 
     bytes_alg = w.algorithmic_bytes
     print(f"Elapsed Time (total):      {gpu_ms / 1e3:.4f} seconds\n"
@@ -289,11 +371,18 @@ def main(argv=None) -> int:
           f"{PEAK_TFLOPS} peak)\n"
           f"Memory Throughput:         {bytes_alg / (ms_per_step * 1e-3) / 1e9:.2f} GB/s "
           f"(algorithmic bytes, decimal GB)\n"
-          f"Median single launch:      {med_ms:.4f} ms", file=sys.stderr, flush=True)
+          f"Median single launch:      {med_ms:.4f} ms\n"
+          f"Engine clock (sampled):    {clk.get('sclk_mhz')} MHz", file=sys.stderr, flush=True)
 
     traffic = load_traffic(w.name)
-    roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_TFLOPS, "traffic": traffic,
+    gbs = bytes_alg / (ms_per_step * 1e-3) / 1e9
+    if w.flops / bytes_alg >= PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        bound = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / PEAK_TFLOPS}
+    else:  # below the ridge (about 315 FLOP per byte): the algorithmic bytes bound it
+        bound = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": gbs / HBM_PEAK_GBS}
+    roofline = {**bound, "traffic": traffic,
                 "kernel": kernel_name(w),
                 "flops_per_launch": w.flops, "avg_launch_ms": ms_per_step,
                 "median_launch_ms": med_ms, "algorithmic_bytes_per_launch": bytes_alg,
@@ -314,8 +403,11 @@ def main(argv=None) -> int:
                    "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
                    "parallelism": "single GPU"},
         "pct_of_peak": 100 * tflops / PEAK_TFLOPS,
+        **clock_fields(tflops, PEAK_TFLOPS, clk),
+        "settle": settled,
         "wall_s": wall,
         "roofline": roofline,
+        "cold": cold,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -336,18 +428,21 @@ def calibrate_copy(torch, dev, stream):
 
 def timed(step, stream, torch, steps: int, warmup: int):
     """W untimed steps, then K timed back-to-back on `stream` (HIP events on
-    that stream); returns (ms per step, wall seconds, median single-launch ms)."""
+    that stream), with the engine clock sampled meanwhile; returns (ms per
+    step, wall seconds, median single-launch ms, clock report)."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    sampler = ClockSampler()
+    with sampler:
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * min(steps, 20))]
     for i in range(0, len(evs), 2):
@@ -356,7 +451,59 @@ def timed(step, stream, torch, steps: int, warmup: int):
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     med = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]))
-    return ms, wall, med
+    return ms, wall, med, sampler.report()
+
+
+COLD_MAX_BYTES = 64 << 20  # workloads below this get the cold-cache leg by default
+SCRUB_BYTES = 512 << 20    # larger than the 256 MB last-level cache (MALL) plus the L2s
+
+
+def cold_timing(step, stream, torch, dev, alg_bytes: int, reps: int = 20) -> dict:
+    """Each launch timed on its own after a 512 MiB scrub write has evicted
+    the inputs from L2 and the MALL: the cold-cache rate of a small workload
+    whose inputs otherwise stay cached between back-to-back launches."""
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    per = []
+    with torch.cuda.stream(stream):
+        for i in range(reps + 2):
+            scrub.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            e1.synchronize()
+            if i >= 2:
+                per.append(e0.elapsed_time(e1))
+    del scrub
+    med = float(np.median(per))
+    return {"median_launch_ms": med, "min_launch_ms": float(min(per)), "launches": len(per),
+            "algorithmic_gbs": alg_bytes / (med * 1e-3) / 1e9,
+            "scrub_bytes": SCRUB_BYTES,
+            "note": "each launch alone after a 512 MiB scrub write (L2 and MALL evicted)"}
+
+
+def settle(torch, dev, stream, seconds: float) -> dict:
+    """Brings the GPU out of idle before the warm-up steps: plain device
+    fills of a 256 MiB buffer for `seconds`. From idle the power manager takes
+    tens of milliseconds of sustained load to raise the engine clock (the
+    first launches of the long workload after idle run at 1.7x their steady
+    duration), so without this a short warm-up leaves the clock ramp inside
+    the timed steps. The fills are not the attention kernel: the warm-up and
+    timed steps stay exactly W and K launches of it."""
+    if seconds <= 0:
+        return {"seconds": 0.0, "fills": 0}
+    buf = torch.empty(1 << 26, dtype=torch.float32, device=dev)
+    n = 0
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                buf.fill_(float(n))
+                n += 1
+            stream.synchronize()
+    del buf
+    return {"seconds": round(time.perf_counter() - t0, 3), "fills": n,
+            "what": "256 MiB device fills before the warm-up steps (engine clock out of idle)"}
 
 
 def bench_fp8(args, torch, fa, w) -> int:
@@ -377,7 +524,8 @@ def bench_fp8(args, torch, fa, w) -> int:
     torch.cuda.synchronize()
     if args.calibrate_copy:
         calibrate_copy(torch, dev, stream)
-    ms, wall, med = timed(step, stream, torch, args.steps, args.warmup)
+    settled = settle(torch, dev, stream, args.settle_s)
+    ms, wall, med, clk = timed(step, stream, torch, args.steps, args.warmup)
     assert bool(torch.isfinite(lse).all()), "non-finite output"
     tflops = w.flops / (ms * 1e-3) / 1e12
     print(f"Average Time Per Step:     {ms:.4f} ms\n"
@@ -404,6 +552,8 @@ def bench_fp8(args, torch, fa, w) -> int:
                    "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
                    "descales": list(ds), "parallelism": "single GPU"},
         "pct_of_peak": 100 * tflops / PEAK_TFLOPS_FP8,
+        **clock_fields(tflops, PEAK_TFLOPS_FP8, clk),
+        "settle": settled,
         "wall_s": wall,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -434,16 +584,8 @@ def bench_varlen(args, torch, fa) -> int:
                          total, total, w.D, int(w.causal), w.scale, stream.cuda_stream,
                          W.DTYPE_CODE[w.dtype], st)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    settled = settle(torch, dev, stream, args.settle_s)
+    ms, wall, med, clk = timed(step, stream, torch, args.steps, args.warmup)
     assert bool(torch.isfinite(lse).all()), "non-finite output"
     tflops = w.flops() / (ms * 1e-3) / 1e12
     print(f"Average Time Per Step:     {ms:.4f} ms\n"
@@ -460,9 +602,13 @@ def bench_varlen(args, torch, fa) -> int:
                                f"D={w.D} {w.dtype}, packed [total, H, D]",
                    "lengths": [int(x) for x in L], "parallelism": "single GPU"},
         "pct_of_peak": 100 * tflops / PEAK_TFLOPS,
+        **clock_fields(tflops, PEAK_TFLOPS, clk),
+        "settle": settled,
+        "wall_s": wall,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_TFLOPS, "traffic": None,
-                     "flops_per_launch": w.flops(), "avg_launch_ms": ms},
+                     "flops_per_launch": w.flops(), "avg_launch_ms": ms,
+                     "median_launch_ms": med},
     }
     print(json.dumps(out), flush=True)
     return 0

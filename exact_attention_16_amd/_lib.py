@@ -20,14 +20,6 @@ LIB_PATH = os.path.join(HERE, "libfa_fwd.so")
 FA_F16 = 0
 FA_BF16 = 1
 
-# kernel choice of fa_fwd_diag
-VARIANT_AUTO = 0
-VARIANT_FOUR_WAVE = 1
-VARIANT_PING_PONG = 2
-VARIANT_TWO_BLOCK = 3
-VARIANT_INTERLEAVE = 4
-VARIANT_PERSISTENT = 5
-
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_DIM", -3: "FA_ERR_UNSUPPORTED",
     -4: "FA_ERR_ALIGN", -5: "FA_ERR_SCALE", -6: "FA_ERR_ALIAS", -7: "FA_ERR_HIP",
@@ -43,7 +35,6 @@ SIGNATURES = {
     "fa_fwd": (_I, _FWD_ARGS + [_I]),
     "fa_fwd_f16": (_I, _FWD_ARGS),
     "fa_fwd_bf16": (_I, _FWD_ARGS),
-    "fa_fwd_diag": (_I, _FWD_ARGS + [_I, _I, _I, _P]),
     "fa_fwd_strided": (_I, [_P] * 5 + [_I] * 6 + [_F, _P, _I, _P]),
     "fa_fwd_varlen": (_I, [_P] * 7 + [_I] * 8 + [_F, _P, _I, _P]),
     "fa_fwd_kt": (_I, _FWD_ARGS + [_I]),
@@ -100,13 +91,6 @@ def fa_fwd_f16(q, k, v, o, lse, B, H, S, D, causal, scale, stream, check=True):
 def fa_fwd_bf16(q, k, v, o, lse, B, H, S, D, causal, scale, stream, check=True):
     st = load().fa_fwd_bf16(q, k, v, o, lse, B, H, S, D, int(causal), scale, stream)
     return _check(st, "fa_fwd_bf16") if check else st
-
-
-def fa_fwd_diag(q, k, v, o, lse, B, H, S, D, causal, scale, stream, dtype,
-                threshold_log2, variant, rescale_events, check=True):
-    st = load().fa_fwd_diag(q, k, v, o, lse, B, H, S, D, int(causal), scale, stream,
-                            dtype, threshold_log2, variant, rescale_events)
-    return _check(st, "fa_fwd_diag") if check else st
 
 
 def _strides(values, n):
@@ -173,9 +157,39 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _check_inputs(q, k, v, dims):
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+def _check_outputs(q, out, lse, o_shape, lse_shape, o_dtype):
+    """out and lse as the kernel writes them: out of o_dtype and o_shape, lse
+    float32 of lse_shape, both on q's device. Checked before any launch: the
+    kernel derives the byte sizes it writes from the element types, which the
+    C-side span checks cannot see."""
+    import torch
+    if out is not None:
+        if out.dtype != o_dtype:
+            raise ValueError(f"out must be {o_dtype}, not {out.dtype}")
+        if tuple(out.shape) != tuple(o_shape):
+            raise ValueError(f"out must have shape {tuple(o_shape)}, not {tuple(out.shape)}")
+        if out.device != q.device:
+            raise ValueError(f"out must be on {q.device}, not {out.device}")
+        if out.dim() and out.stride(-1) != 1:
+            raise ValueError("out's last dimension (D) must be contiguous")
+    if lse is not None:
+        if lse.dtype != torch.float32:
+            raise ValueError(f"lse must be float32, not {lse.dtype}")
+        if tuple(lse.shape) != tuple(lse_shape):
+            raise ValueError(f"lse must have shape {tuple(lse_shape)}, not {tuple(lse.shape)}")
+        if lse.device != q.device:
+            raise ValueError(f"lse must be on {q.device}, not {lse.device}")
+
+
+def _check_devices(q, *others):
+    if not q.is_cuda:
         raise ValueError("q, k, v must be device tensors")
+    for t in others:
+        if t.device != q.device:
+            raise ValueError(f"every tensor must be on {q.device}, not {t.device}")
+
+
+def _check_structure(q, k, v, dims):
     if not (q.dim() == k.dim() == v.dim() == dims):
         raise ValueError(f"q, k, v must have {dims} dimensions")
     if not (q.dtype == k.dtype == v.dtype):
@@ -200,7 +214,7 @@ def attention(q, k, v, causal: bool, scale: float | None = None, out=None, lse=N
     call returns without synchronising.
     """
     import torch
-    _check_inputs(q, k, v, 4)
+    _check_structure(q, k, v, 4)
     if layout == "bhsd":
         B, H, Sq, D = q.shape
         Sk = k.shape[2]
@@ -215,6 +229,8 @@ def attention(q, k, v, causal: bool, scale: float | None = None, out=None, lse=N
         perm = (0, 2, 1)
     else:
         raise ValueError(f"unknown layout {layout!r}")
+    _check_outputs(q, out, lse, q.shape, (B, H, Sq), q.dtype)
+    _check_devices(q, k, v)
     if scale is None:
         scale = D ** -0.5
     if out is None:
@@ -255,17 +271,19 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
     aligned bottom-right within each sequence.
     """
     import torch
-    _check_inputs(q, k, v, 3)
+    _check_structure(q, k, v, 3)
     total_q, H, D = q.shape
     total_k = k.shape[0]
     if k.shape[1] != H or k.shape[2] != D:
         raise ValueError("k, v must be [total_k, H, D] with q's H and D")
     for cu in (cu_seqlens_q, cu_seqlens_k):
-        if not cu.is_cuda or cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
             raise ValueError("cu_seqlens must be contiguous int32 device tensors")
     if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 offsets")
     B = cu_seqlens_q.numel() - 1
+    _check_outputs(q, out, lse, (total_q, H, D), (H, total_q), q.dtype)
+    _check_devices(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if scale is None:
         scale = D ** -0.5
     if out is None:
@@ -298,7 +316,7 @@ def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
     (default: torch's current stream) without synchronising.
     """
     import torch
-    _check_inputs(q, k, v, 4)
+    _check_structure(q, k, v, 4)
     if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
         raise TypeError(f"8-bit inputs must be float8_e4m3fn or uint8 codes, not {q.dtype}")
     if q.shape != k.shape:
@@ -306,6 +324,8 @@ def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("8-bit inputs must be contiguous [B, H, S, D]")
     B, H, S, D = q.shape
+    _check_outputs(q, out, lse, (B, H, S, D), (B, H, S), torch.bfloat16)
+    _check_devices(q, k, v)
     if scale is None:
         scale = D ** -0.5
     if out is None:
@@ -331,8 +351,6 @@ def attention_kt(q, kt, v, causal: bool, scale: float | None = None, out=None, l
     [B, H, D, S] (S a multiple of 8). Returns (o, lse) as :func:`attention`.
     """
     import torch
-    if not (q.is_cuda and kt.is_cuda and v.is_cuda):
-        raise ValueError("q, kt, v must be device tensors")
     if not (q.dtype == kt.dtype == v.dtype):
         raise ValueError("q, kt, v must share one dtype")
     B, H, S, D = q.shape
@@ -340,6 +358,8 @@ def attention_kt(q, kt, v, causal: bool, scale: float | None = None, out=None, l
         raise ValueError("kt must be [B, H, D, S] and v [B, H, S, D] for q [B, H, S, D]")
     if not (q.is_contiguous() and kt.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, kt, v must be contiguous")
+    _check_outputs(q, out, lse, q.shape, (B, H, S), q.dtype)
+    _check_devices(q, kt, v)
     if scale is None:
         scale = D ** -0.5
     if out is None:

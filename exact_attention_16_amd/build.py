@@ -1,8 +1,14 @@
-"""Build the gfx950 HIP library in-tree: exact_attention_16_amd/libfa_fwd.so.
+"""Build the gfx950 HIP libraries in-tree:
+
+* exact_attention_16_amd/libfa_fwd.so -- the product library (include/fa_fwd.h);
+* exact_attention_16_amd/libfa_fwd_diag.so -- the diagnostic library the tests
+  load beside it (include/fa_fwd_diag.h: the same kernels with a
+  rescale-event counter, both lag thresholds, and a forced kernel choice).
 
 Usage: python -m exact_attention_16_amd.build [--verbose] [--save-temps DIR]
 
-Compiles every time it is called. The code object targets gfx950 only.
+Compiles both (in parallel) every time it is called. The code objects target
+gfx950 only.
 Packed fp32 VALU instructions are disabled for the device code
 (-packed-fp32-ops); the host pass warns that it does not know the feature,
 which is harmless.
@@ -19,6 +25,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_fwd_fp8.hip")]
 OUT = os.path.join(HERE, "libfa_fwd.so")
+DIAG_SRCS = [os.path.join(HERE, "csrc", "fa_fwd_diag.hip")]
+DIAG_OUT = os.path.join(HERE, "libfa_fwd_diag.so")
 ARCH = "gfx950"
 
 
@@ -40,28 +48,43 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False, save_temps: str | None = None, resource_usage: bool = False) -> str:
-    tmp = OUT + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *SRCS, "-o", tmp]
+def _command(srcs, out, save_temps, resource_usage):
+    cmd = [hipcc(), *compile_flags(), *srcs, "-o", out + ".tmp"]
     if resource_usage:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     if save_temps:
-        os.makedirs(save_temps, exist_ok=True)
-        cmd += [f"-save-temps={'obj'}"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    cwd = save_temps or None
+        cmd += ["-save-temps=obj"]
+        cmd[cmd.index("-o") + 1] = os.path.abspath(out + ".tmp")
+    return cmd
+
+
+def build(verbose: bool = False, save_temps: str | None = None, resource_usage: bool = False,
+          diag: bool = True) -> str:
+    """Compile the product library (and the diagnostic one unless diag=False);
+    returns the product library's path."""
+    jobs = [(SRCS, OUT)] + ([(DIAG_SRCS, DIAG_OUT)] if diag else [])
     if save_temps:
-        cmd[cmd.index("-o") + 1] = os.path.abspath(tmp)
-    r = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
-    out = (r.stdout or "") + (r.stderr or "")
-    # the host pass does not know the device-only target feature
-    out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
-    if verbose or resource_usage:
-        print(out, flush=True)
-    os.replace(tmp, OUT)
+        os.makedirs(save_temps, exist_ok=True)
+    procs = []
+    for srcs, out in jobs:
+        cmd = _command(srcs, out, save_temps, resource_usage)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, subprocess.Popen(cmd, cwd=save_temps or None, stdout=subprocess.PIPE,
+                                            stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for out, p in procs:
+        text, _ = p.communicate()
+        # the host pass does not know the device-only target feature
+        text = "\n".join(l for l in (text or "").splitlines() if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed.append(f"{os.path.basename(out)}: hipcc failed ({p.returncode}):\n{text}")
+            continue
+        if verbose or resource_usage:
+            print(text, flush=True)
+        os.replace(out + ".tmp", out)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return OUT
 
 
@@ -70,8 +93,9 @@ def main(argv=None) -> int:
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true")
     ap.add_argument("--save-temps", default=None)
+    ap.add_argument("--no-diag", action="store_true", help="build the product library only")
     a = ap.parse_args(argv)
-    p = build(a.verbose, a.save_temps, a.resource_usage)
+    p = build(a.verbose, a.save_temps, a.resource_usage, diag=not a.no_diag)
     print(p)
     return 0
 

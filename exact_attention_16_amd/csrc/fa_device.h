@@ -1,12 +1,14 @@
 // Device building blocks shared by the gfx950 attention-forward kernels:
 // vector types, lane exchanges, buffer descriptors, LDS pointer types,
-// barriers and waits, scheduling patterns, and the Problem a launch solves.
+// barriers and waits, scheduling patterns, the rows of a Problem (fa_problem.h)
+// and the per-row softmax state every wave type shares.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "fa_layout.h"
+#include "fa_problem.h"
 
 namespace fa {
 
@@ -20,8 +22,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLog2e = 1.442695040888963407f;
 // Word 3 of a raw (untyped, stride 0) gfx9 buffer descriptor.
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -92,21 +92,6 @@ template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0x0070 | N);
 }
 
-// Scheduling pattern for one region: DS0 LDS reads up front, then REPS
-// times {one MFMA, V1 VALU, DS LDS reads, one MFMA, V2 VALU}.
-template <int DS0, int REPS, int V1, int DS, int V2>
-__device__ __forceinline__ void interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
-#pragma unroll
-  for (int i = 0; i < REPS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, V1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, V2, 0);
-  }
-}
-
 // Scheduling pattern for one MFMA loop: DS0 LDS reads up front, then N
 // times {one MFMA, DS LDS reads}, so that each MFMA's operands are read
 // several MFMAs ahead of it. (Left to itself the scheduler reads them just
@@ -133,33 +118,6 @@ __device__ __forceinline__ void mix() {
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
   }
 }
-
-// What one launch computes, passed to the kernels by value. Strides are in
-// elements; a row is D contiguous elements. Without per-sequence offsets
-// (cuq == nullptr) sequence b, head h has Sq query rows starting at
-// q + b*qb + h*qh (row stride qs) and Sk key rows in k and v likewise; o has
-// q's row count and lse is Sq floats at lse + b*lb + h*lh. With offsets,
-// sequence b's query rows are token rows cuq[b] .. cuq[b+1]-1 (so its rows
-// start at q + cuq[b]*qs + h*qh, lse + h*lh + cuq[b]) and its key rows are
-// token rows cuk[b] .. cuk[b+1]-1; the kernel clamps both ranges to the
-// totq / totk token rows the tensors hold and the lengths to Sq / Sk.
-struct Problem {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
-  long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os, lb, lh;
-  const int* cuq;
-  const int* cuk;
-  int totq, totk;
-  int B, H, Sq, Sk;
-  int nqt;  // query tiles per (sequence, head) for the kernel's block of rows
-  float c;  // scale * log2(e) (8-bit inputs: times the Q and K descales)
-  unsigned long long* events;
-  float vscale;  // 8-bit inputs: the V descale, applied to O at the end
-  int hgroup;    // causal: heads an XCD takes together (block_to_tile)
-};
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 

@@ -1,6 +1,7 @@
-// The eight-wave interleaved work-group, written once for any wave type W
-// (the same interface as pp_body in fa_pingpong.h, plus il_schedule: the
-// scheduling pattern of the softmax-with-QK block).
+// The eight-wave interleaved work-group of the 8-bit kernel
+// (fa_fwd_fp8.hip), written over a wave type W with the interface pp_body in
+// fa_pingpong.h uses, plus il_schedule: the scheduling pattern of the
+// softmax-with-QK block.
 //
 // All eight waves (two per SIMD) run the same code. Per KV tile j a wave
 //   * issues its share of DMA pair j (K(j+2) and V(j+1)), waits until its

@@ -1,0 +1,240 @@
+// The 16-bit attention-forward kernels for gfx950 and their launch
+// templates, shared by the product library (fa_fwd.hip: the production
+// instantiations) and the diagnostic library (fa_fwd_diag.hip: the same
+// kernels instantiated with a rescale-event counter and a lag threshold of
+// 0 or 8, plus the persistent form of the ping-pong kernel).
+//
+//  * fa_fwd_pp (eight waves, 256 query rows; work-group body in
+//    fa_pingpong.h): two wave groups whose slots alternate between an MFMA
+//    phase and a softmax phase, so each SIMD always holds one multiplying
+//    and one exponentiating wave; K/V in three LDS stages, two tiles ahead.
+//  * fa_fwd_k4 (four waves, 128 query rows), for grids too small to fill the
+//    chip with 256-row tiles: each wave overlaps the next tile's K.Q^T (and,
+//    at D=64, the previous tile's P.V) with its own current softmax.
+//  * fa_fwd_pp_kt: the ping-pong body on a K given transposed ([D, S]).
+//  * fa_fwd_pp_persist: the ping-pong body in persistent form.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa_fwd.h"
+#include "fa_device.h"
+#include "fa_pingpong.h"
+#include "fa_wave.h"
+
+namespace fa {
+
+// ------------------------------------------------- eight-wave ping-pong
+template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_pp(const Problem P) {
+  pp_body<Wave<T, Cfg8<D>, CAUSAL, THR, DIAG>>(P);
+}
+
+// ------------------------------------------------- persistent ping-pong
+template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_pp_persist(const Problem P) {
+  pp_persistent<Wave<T, Cfg8<D>, CAUSAL, THR, DIAG>>(P);
+}
+
+// ------------------------------------------------- K given transposed
+// The ping-pong work-group on a [D, S] K: 64-key tiles at D = 128 and
+// 128-key tiles at D = 64, so that a transposed K tile has 128- or 256-byte
+// rows like a V tile.
+template <int D> using CfgKT = Cfg<D, 8, (D == 64 ? 128 : 64)>;
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_pp_kt(const Problem P) {
+  pp_body<Wave<T, CfgKT<D>, CAUSAL, 8, false, true>>(P);
+}
+
+
+// ------------------------------------------------------------ four-wave
+// Register pipeline depth per head dimension. D=64: three stages (S(j+1),
+// P(j-1).V(j-1) and softmax(j) in one block) fit two waves per SIMD. D=128:
+// two stages (the history from the tile max alone, the rare rescale, then
+// one block with the exponentials, P(j).V(j) and S(j+1)); the other wave on
+// the SIMD covers the rest.
+template <int D> struct Pipe { static constexpr bool three = D == 64; };
+
+template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_k4(const Problem P) {
+  using C = Cfg4<D>;
+  using W = Wave<T, C, CAUSAL, THR, DIAG>;
+  constexpr bool P3 = Pipe<D>::three;
+  constexpr int NKB = W::NKB, NKC = W::NKC;
+  constexpr int TB = C::tileBytes;
+  // one array per stage, V stages first in name order (as in fa_fwd_pp)
+  __shared__ __attribute__((aligned(1024))) char b_kstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char b_kstage1[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage0[TB];
+  __shared__ __attribute__((aligned(1024))) char a_vstage1[TB];
+  lds_char* const lk0 = (lds_char*)b_kstage0;
+  lds_char* const lk1 = (lds_char*)b_kstage1;
+  lds_char* const lv0 = (lds_char*)a_vstage0;
+  lds_char* const lv1 = (lds_char*)a_vstage1;
+
+  W w;
+  if (!w.init(P)) return;
+  const int ntiles = w.group_tiles();
+  const int nw = w.wave_tiles();
+
+  f32x16 sA[NKB], sB[NKB];  // S(j) lives in sA for even j, sB for odd j
+  u32x4 pA[NKC], pB[NKC];   // P(j) likewise (only pA is used with two stages)
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) pB[kc] = (u32x4){};  // P(-1) = 0
+
+  // ---- prologue: K(0), K(1) (and V(0) with two stages) in LDS; S(0) --------
+  // With three stages iteration 0 runs the steady-state block with P(-1) = 0
+  // against V buffer 1, so that buffer must hold finite values (0 * NaN
+  // would poison O).
+  w.dma_k(lk0, 0);
+  if (ntiles > 1) w.dma_k(lk1, 1);
+  if constexpr (P3) {
+#pragma unroll
+    for (int i = 0; i < TB / (16 * C::threads); ++i)
+      *(__attribute__((address_space(3))) u32x4*)(lv1 + 16 * (threadIdx.x + i * C::threads)) =
+          (u32x4){};
+  } else {
+    w.dma_v(lv0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (nw > 0) w.qk(sA, lk0);
+  __syncthreads();  // b_kstage0 is refilled with K(2) in iteration 0
+
+  // ---- iteration j (PH = j % 2). DMA first (K(j+2); V(j) with three stages,
+  // V(j+1) with two). A wave that still has tile j then computes; at its
+  // last tile the S(j+1) it computes is not used. With three stages
+  // iteration nw only drains P(nw-1).V(nw-1). The wave keeps issuing its
+  // share of the DMA and the barriers until the work-group's last tile.
+  auto iter = [&](auto ph, int j) {
+    constexpr int PH = decltype(ph)::value;
+    f32x16(&scur)[NKB] = pick<PH>(sB, sA);
+    f32x16(&snext)[NKB] = pick<PH>(sA, sB);
+    u32x4(&pcur)[NKC] = P3 ? pick<PH>(pB, pA) : pA;
+    u32x4(&pprev)[NKC] = pick<PH>(pA, pB);
+    lds_char* k_next = PH ? lk0 : lk1;  // holds K(j+1)
+    lds_char* k_dma = PH ? lk1 : lk0;   // receives K(j+2)
+    lds_char* v_cur = PH ? lv1 : lv0;   // V(j) (two stages) / receives V(j) (three)
+    lds_char* v_oth = PH ? lv0 : lv1;   // V(j-1) (three stages) / receives V(j+1) (two)
+    if constexpr (P3) {
+      if (j < ntiles) w.dma_v(v_cur, j);
+    } else {
+      if (j + 1 < ntiles) w.dma_v(v_oth, j + 1);
+    }
+    if (j + 2 < ntiles) w.dma_k(k_dma, j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (j < nw) {
+      const int kv0 = j * W::BN;
+      if (w.needs_mask(kv0)) w.mask(scur, kv0);
+      if constexpr (P3) {
+        // one block: P(j-1).V(j-1) and S(j+1) MFMAs under softmax(j); the
+        // rescale of O by softmax(j)'s history follows P(j-1).V(j-1). P(j)
+        // and the row sum are pinned in the block instead of sinking past
+        // the rescale branch.
+        w.pv(pprev, v_oth);
+        const float hist = w.softmax_max(scur);
+        w.softmax_exp(scur, pcur);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(pcur[kc]));
+        asm volatile("" : "+v"(w.lsum));
+        w.qk(snext, k_next);
+        w.rescale(j, hist);
+      } else {
+        // the history is known from the tile max alone: rescale O first,
+        // then one block with the exponentials, P(j).V(j) (each 16-key chunk
+        // as soon as its P is packed) and the S(j+1) MFMAs
+        const float hist = w.softmax_max(scur);
+        w.rescale(j, hist);
+        w.softmax_exp(scur, pcur);
+        w.pv(pcur, v_cur);
+        w.qk(snext, k_next);
+      }
+    } else if (P3 && j == nw) {
+      w.pv(pprev, v_oth);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  const int niter = P3 ? ntiles + 1 : ntiles;
+  int j = 0;
+  for (; j + 1 < niter; j += 2) {
+    iter(IC<0>{}, j);
+    iter(IC<1>{}, j + 1);
+  }
+  if (j < niter) iter(IC<0>{}, j);
+
+  w.epilogue(P.events);
+}
+
+// ------------------------------------------------------------------- host
+
+// Kernel choice: the ping-pong kernel when its 256-row tiles give at least
+// one work-group per compute unit, else the four-wave kernel.
+constexpr long long kPingPongMinGroups = 256;
+
+// Kernel variants (the diagnostic entry point can force one; 3 and 4 are
+// retired kernel numbers)
+enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kPersistent = 5 };
+
+template <int D> static inline bool use_pingpong(int BH, int S, int variant) {
+  if (variant == kFourWave) return false;
+  if (variant == kPingPong || variant == kPersistent) return true;
+  return (long long)num_q_tiles(S, Cfg8<D>::BM) * BH >= kPingPongMinGroups;
+}
+
+// Work-groups of the persistent kernel: one per CU of the current device,
+// rounded down to a multiple of the 8 XCDs.
+static inline int persistent_groups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus / 8 * 8;
+}
+
+// One launch of the kernel `variant` selects for a filled, validated Problem.
+template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
+static int launch_one(Problem P, hipStream_t stream, int variant) {
+  const int BH = P.B * P.H;
+  if (DIAG && variant == kPersistent) {
+    if constexpr (DIAG) {
+      P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);
+      const int g = persistent_groups();
+      if (g <= 0) return FA_ERR_HIP;
+      hipLaunchKernelGGL((fa_fwd_pp_persist<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)g),
+                         dim3(Cfg8<D>::threads), 0, stream, P);
+    }
+  } else if (use_pingpong<D>(BH, P.Sq, variant)) {
+    P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);
+    hipLaunchKernelGGL((fa_fwd_pp<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+                       dim3(Cfg8<D>::threads), 0, stream, P);
+  } else {
+    P.nqt = num_q_tiles(P.Sq, Cfg4<D>::BM);
+    hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+                       dim3(Cfg4<D>::threads), 0, stream, P);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <typename T, int THR, bool DIAG>
+static int launch(const Problem& P, int D, int causal, hipStream_t st, int variant) {
+  if (D == 64)
+    return causal ? launch_one<T, 64, true, THR, DIAG>(P, st, variant)
+                  : launch_one<T, 64, false, THR, DIAG>(P, st, variant);
+  return causal ? launch_one<T, 128, true, THR, DIAG>(P, st, variant)
+                : launch_one<T, 128, false, THR, DIAG>(P, st, variant);
+}
+
+}  // namespace fa

@@ -53,18 +53,10 @@ template <int D_, int NW_, int BN_, int RPW_ = kRowsPerWave, int ES_ = 2> struct
 // The kernels: four waves (128 query rows) with a two- or three-stage
 // register pipeline per wave, for grids too small to fill the chip with
 // 256-row tiles; eight waves (256 rows) in two groups that alternate MFMA
-// and softmax phases (ping-pong); four waves of 64 rows (256 rows). The
-// ping-pong kernel uses 128-key tiles at D=64 so that an MFMA phase (32
-// MFMAs) balances a softmax phase.
+// and softmax phases (ping-pong). The ping-pong kernel uses 128-key tiles at
+// D=64 so that an MFMA phase (32 MFMAs) balances a softmax phase.
 template <int D> using Cfg4 = Cfg<D, 4, 64>;
 template <int D> using Cfg8 = Cfg<D, 8, (D == 64 ? 128 : 96)>;
-// Four waves of two 32-row blocks each (256 rows): every K/V operand read
-// from LDS feeds both blocks' MFMAs, half the LDS traffic per FLOP of the
-// one-block kernels. 32-key tiles keep both blocks' S and P in registers.
-template <int D> using CfgW2 = Cfg<D, 4, 32, 64>;
-// Eight waves of 32 rows (256 rows), each interleaving its own softmax with
-// its next tile's MFMAs; 64-key tiles keep two S tiles in registers.
-template <int D> using CfgIL = Cfg<D, 8, 64>;
 
 // ------------------------------------------------------- work decomposition
 // One work-group per (Q tile, batch*head). Work-group ids are dealt to the 8
@@ -112,7 +104,9 @@ FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh
   *qt = causal ? (nqt - 1 - ord) : ord;
 }
 
-FA_HD int num_q_tiles(int S, int BM) { return (S + BM - 1) / BM; }
+// ceil(S / BM) for S >= 0, without forming S + BM - 1 (which overflows int
+// for S near INT_MAX)
+FA_HD int num_q_tiles(int S, int BM) { return S / BM + (S % BM != 0); }
 
 // Work item of a persistent work-group b (of G, a multiple of 8) at round k:
 // a snake over the ranks of its XCD (see pp_persistent); -1 past the last.

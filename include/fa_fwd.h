@@ -59,7 +59,8 @@ typedef enum {
   FA_ERR_SCALE = -5,       /* scale not finite or not > 0                   */
   FA_ERR_ALIAS = -6,       /* o or lse overlaps another buffer              */
   FA_ERR_HIP = -7,         /* the HIP runtime rejected the launch           */
-  FA_ERR_ARG = -8,         /* causal not 0/1, or a bad diagnostic argument  */
+  FA_ERR_ARG = -8,         /* causal not 0/1 (or a bad argument of the
+                              diagnostic library's fa_fwd_diag)             */
   FA_ERR_LAYOUT = -9       /* a stride is negative, a row stride < D, or an
                               output's rows overlap each other             */
 } fa_status_t;
@@ -73,7 +74,8 @@ typedef enum {
  *   B, H, S  >= 0; B*H*S == 0 is a no-op returning FA_OK (pointers unused).
  *            Any S >= 1 is accepted (a ragged last tile is masked).
  *            Limits: S*D*2 < 2^31 (one head's K/V/O addressed with 32-bit
- *            offsets), B*H*S*D <= 2^40, B*H*ceil(S/128) < 2^31.
+ *            offsets), H*S*D <= 2^40 and B*H*S*D <= 2^40,
+ *            B*H*ceil(S/128) < 2^31; beyond them FA_ERR_DIM.
  *   D        head dimension, 64 or 128
  *   causal   0 = every key visible; 1 = key j visible to row i iff j <= i
  *   scale    multiplier of q.k; finite and > 0 (typically 1/sqrt(D)).
@@ -118,7 +120,9 @@ int fa_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse
  *   other arguments as for fa_fwd.
  *
  * Limits: Sq*ss*2 and Sk*ss*2 < 2^31 for each tensor's row stride ss (one
- * (sequence, head) addressed with 32-bit offsets). Errors: negative or
+ * (sequence, head) addressed with 32-bit offsets); every stride <= 2^40
+ * elements, and each tensor's span at most 2^40 elements (FA_ERR_DIM;
+ * checked before any arithmetic that could overflow). Errors: negative or
  * overlapping-output strides FA_ERR_LAYOUT; strides not multiples of 8
  * FA_ERR_ALIGN; o or lse sharing bytes with q, k, v or each other (by the
  * byte ranges the strides span) FA_ERR_ALIAS; the rest as for fa_fwd.
@@ -159,41 +163,6 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
                   int D, int causal, float scale, hipStream_t stream, int dtype,
                   const long long* strides);
-
-/*
- * fa_fwd_diag -- diagnostic variant of fa_fwd for tests.
- *
- * Same arguments and result as fa_fwd, plus:
- *   threshold_log2   how far (log2 units of the scaled logit) the running
- *                    max may lag before the accumulator is rescaled:
- *                    8 (the production setting) or 0 (rescale on every
- *                    increase, the eager FlashAttention-2 rule).
- *   rescale_events   device pointer to one unsigned 64-bit counter, owned
- *                    by the caller; the kernel atomically adds the number
- *                    of (query row, KV tile) pairs whose running max moved
- *                    after the row's first tile. Not cleared by the library.
- *   variant          which kernel runs: 0 = the one fa_fwd picks for this
- *                    shape, 1 = the four-wave kernel (128 query rows per
- *                    work-group), 2 = the eight-wave ping-pong kernel (256
- *                    rows), 3 = the four-wave kernel with two 32-row blocks
- *                    per wave (256 rows, 32-key tiles), 4 = the eight-wave
- *                    kernel in which every wave overlaps its own softmax
- *                    with its next tile's MFMAs (256 rows, 64-key tiles;
- *                    the "interleaved" kernel), 5 = the eight-wave
- *                    ping-pong kernel in persistent form (one work-group
- *                    per CU of the current device, rounded down to a
- *                    multiple of 8, each running query tiles in turn).
- *                    Every variant computes the same result, to rounding;
- *                    the choice only affects speed.
- * It runs separate, instrumented instantiations of the same kernels.
- * Invalid threshold_log2 or variant: FA_ERR_ARG; NULL rescale_events:
- * FA_ERR_NULL; rescale_events not 8-byte aligned: FA_ERR_ALIGN; the CU
- * count of the current device not readable (variant 5): FA_ERR_HIP.
- */
-int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
-                int B, int H, int S, int D, int causal, float scale,
-                hipStream_t stream, int dtype, int threshold_log2, int variant,
-                unsigned long long* rescale_events);
 
 /*
  * fa_fwd_tile -- the tile shape fa_fwd uses for a call with (B, H, S) at

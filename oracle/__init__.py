@@ -23,9 +23,9 @@ Contents:
 """
 from .attention import (attention_fwd, attention_rows, attention_probs,
                         attention_bruteforce, attention_varlen)
-from .fp8 import attention_fp8, attention_fp8_rows, pv_rounding_bound
+from .fp8 import attention_fp8, pv_rounding_bound
 from .online import online_softmax_attention
 
 __all__ = ["attention_fwd", "attention_rows", "attention_probs",
            "attention_bruteforce", "attention_varlen", "online_softmax_attention",
-           "attention_fp8", "attention_fp8_rows", "pv_rounding_bound"]
+           "attention_fp8", "pv_rounding_bound"]

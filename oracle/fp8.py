@@ -15,10 +15,18 @@ follows is a reading:
 * A fast kernel also rounds the probabilities P to E4M3 before the P V
   product (it runs on the 8-bit matrix units). That rounding is an
   approximation, so the comparison needs a bound: :func:`pv_rounding_bound`.
-  The kernel rounds each probability multiplied by a power of two that keeps
-  the largest at or below 256 (< 448, E4M3's largest) and that is at least
-  ``p_scale`` (2^6 by default: a base that lags the running max by up to two
-  binades, and a fixed factor 2^6, as in the kernel). The row sum and the
+  Reading (the pages fix no 8-bit P): the probabilities live in the range the
+  lagging base gives them, p = 2^(s*c - b) in (0, 2^8] with b allowed to
+  trail the running max by up to 8 binades (hjcheng0602.cn, "Flash Attention
+  CUDA Kernel 优化 ... G6", section "V41: Conditional Scale"); 2^8 is below
+  E4M3's largest value 448, so that range needs no clamping. Within it, a
+  row's largest probability may sit anywhere in [1, 2^8]: at 1 right after a
+  rebase, higher while b lags. The least favourable case for rounding is the
+  smallest, 1 (more of the row's small probabilities then fall below E4M3's
+  normal range), so the bound takes that: ``p_scale`` = 1 by default. An
+  implementation that multiplies the probabilities by a larger power of two
+  before rounding (while keeping them at or below 2^8) only tightens its own
+  error; the bound does not depend on that choice. The row sum and the
   log-sum-exp use the unrounded probabilities.
 
 Bound for one row i and one column d, in the units of the (descaled) V:
@@ -32,7 +40,7 @@ L_i = sum_j exp(X_ij - m_i):
             <= 2^-4 sum_j Pn_ij |V_jd|  +  2^-10 / p_scale * sum_j |V_jd| / L_i
 
 with Pn = P / L the normalised weights. (The factor a probability is
-multiplied by may differ between key tiles as the running max moves; the
+multiplied by may differ between key tiles as the running base moves; the
 relative part does not depend on it and the absolute part only shrinks when
 it is larger than p_scale.)
 """
@@ -41,13 +49,18 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import (_causal_mask, _exp_shifted, _logits, _row_max, _row_sum,
-                        attention_fwd, attention_rows)
+                        attention_fwd)
 
 # E4M3: three mantissa bits (relative half-ulp 2^-4), smallest normal 2^-6,
 # subnormal spacing 2^-9 (absolute half-ulp 2^-10).
 REL_HALF_ULP = 2.0 ** -4
 ABS_HALF_ULP = 2.0 ** -10
-P_SCALE = 64.0
+# The smallest factor the reading allows on a row's probabilities before they
+# are rounded: the largest probability at 1, right after a rebase.
+P_SCALE = 1.0
+# The largest value a scaled probability may take: 2^8, the top of the
+# lagging base's range (V41), below E4M3's largest value 448.
+P_MAX = 256.0
 
 
 def attention_fp8(q: np.ndarray, k: np.ndarray, v: np.ndarray, descale, causal: bool,
@@ -60,13 +73,6 @@ def attention_fp8(q: np.ndarray, k: np.ndarray, v: np.ndarray, descale, causal: 
     dq, dk, dv = (float(x) for x in descale)
     return attention_fwd(np.asarray(q) * dq, np.asarray(k) * dk, np.asarray(v) * dv,
                          causal, scale)
-
-
-def attention_fp8_rows(q, k, v, descale, rows, causal: bool, scale: float):
-    """:func:`attention_fp8` for selected query rows of one head (q, k, v: S x D)."""
-    dq, dk, dv = (float(x) for x in descale)
-    return attention_rows(np.asarray(q) * dq, np.asarray(k) * dk, np.asarray(v) * dv,
-                          rows, causal, scale)
 
 
 def pv_rounding_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, causal: bool,

@@ -48,6 +48,20 @@ import numpy as np
 LOG2E = 1.0 / math.log(2.0)
 
 
+def _rebase(b: np.ndarray, scaled_max: np.ndarray, threshold_log2: float):
+    """Steps 3-4 for one tile: the candidate base max(b, scaled tile max); the
+    base moves only when the candidate exceeds b + threshold. Returns the new
+    base, the history factor 2^(b_old - b_new) (1 where the base stays; 0 on a
+    row's first tile, whose base was -inf) and whether the move counts as a
+    rescale (not on the first tile, where the accumulator is still zero)."""
+    cand = np.maximum(b, scaled_max)
+    rebase = cand > b + threshold_log2
+    with np.errstate(invalid="ignore"):
+        history = np.where(rebase, np.exp2(b - cand), 1.0)
+    counted = rebase & np.isfinite(b)
+    return np.where(rebase, cand, b), history, counted
+
+
 def online_softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                              causal: bool, scale: float, block_n: int = 64,
                              threshold_log2: float = 8.0):
@@ -76,15 +90,11 @@ def online_softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
             j = np.arange(kv0, kv1)
             s = np.where(j[None, :] > rows[:, None], -np.inf, s)
         tile_max = s.max(axis=1)                               # step 2
-        cand = np.maximum(b, tile_max * c)                     # step 3
-        rebase = cand > b + threshold_log2                     # step 4
-        with np.errstate(invalid="ignore"):
-            history = np.where(rebase, np.exp2(b - cand), 1.0)
-        counted = rebase & np.isfinite(b)
+        b_new, history, counted = _rebase(b, tile_max * c, threshold_log2)  # steps 3-4
         rescales += counted
         if counted.any():
             min_history = min(min_history, float(history[counted].min()))
-        b = np.where(rebase, cand, b)
+        b = b_new
         with np.errstate(invalid="ignore"):
             p = np.exp2(s * c - b[:, None])                    # step 5
         p = np.where(np.isneginf(s), 0.0, p)

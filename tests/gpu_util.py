@@ -8,6 +8,7 @@ import torch
 import exact_attention_16_amd as fa
 import oracle
 import workloads as W
+from diag import fa_fwd_diag
 
 # Tolerances stated for this path: max |O_gpu - O| over all elements, and
 # max |lse_gpu - lse|, against the float64 oracle on the same 16-bit inputs.
@@ -30,7 +31,7 @@ def run(qb, kb, vb, dtype, causal, scale, stream=None, variant=None):
     """fa_fwd on the seeded bits; returns device tensors (o, lse).
 
     variant None: fa_fwd (the kernel it picks for the shape). Otherwise
-    fa_fwd_diag with that kernel choice (fa.VARIANT_*), production threshold.
+    fa_fwd_diag with that kernel choice (diag.VARIANT_*), production threshold.
     """
     q, k, v = (to_dev(x, dtype) for x in (qb, kb, vb))
     if variant is None:
@@ -41,7 +42,7 @@ def run(qb, kb, vb, dtype, causal, scale, stream=None, variant=None):
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device())
         ev = torch.zeros(1, dtype=torch.int64, device=device())
         B, H, S, D = q.shape
-        fa.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        B, H, S, D, int(causal), scale, torch.cuda.current_stream().cuda_stream,
                        W.DTYPE_CODE[dtype], 8, variant, ev.data_ptr())
     torch.cuda.synchronize()
@@ -52,10 +53,24 @@ def o_to_f64(o: torch.Tensor) -> np.ndarray:
     return o.float().cpu().numpy().astype(np.float64)
 
 
+def max_abs_err(got, ref) -> float:
+    """max |got - ref| where a NaN anywhere counts as an infinite error (so it
+    can never pass a tolerance) and equal infinities (lse = -inf for a row that
+    sees no key, on both sides) count as no error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    same_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    with np.errstate(invalid="ignore"):
+        d = np.where(same_inf, 0.0, np.abs(got - ref))
+    d = np.where(np.isnan(d), np.inf, d)
+    return float(d.max()) if d.size else 0.0
+
+
 def compare_rows(qb, kb, vb, dtype, causal, scale, o_gpu, lse_gpu, heads_rows):
     """Max errors of the GPU result against the oracle on selected rows.
 
-    heads_rows: iterable of ((b, h), rows). Returns (max_abs_O, max_abs_lse).
+    heads_rows: iterable of ((b, h), rows). Returns (max_abs_O, max_abs_lse);
+    a NaN on either side makes the error infinite.
     """
     eo = el = 0.0
     scale = float(np.float32(scale))  # the value the kernel receives
@@ -65,8 +80,8 @@ def compare_rows(qb, kb, vb, dtype, causal, scale, o_gpu, lse_gpu, heads_rows):
         k = W.decode(kb[b, h], dtype)
         v = W.decode(vb[b, h], dtype)
         o_ref, l_ref = oracle.attention_rows(q, k, v, rows, causal, scale)
-        eo = max(eo, float(np.abs(o_gpu[b, h, rows] - o_ref).max()))
-        el = max(el, float(np.abs(lse_gpu[b, h, rows] - l_ref).max()))
+        eo = max(eo, max_abs_err(o_gpu[b, h, rows], o_ref))
+        el = max(el, max_abs_err(lse_gpu[b, h, rows], l_ref))
     return eo, el
 
 

@@ -676,9 +676,6 @@ static void check_pingpong(int ntiles, int nw, bool one_barrier) {
   CHECK(nread == 2 * 2 * nw, "read count %d for %d wave tiles", nread, nw);
 }
 
-// Replays the four-wave two-block kernel: one group, iteration j issues
-// K(j+2) and V(j+1) (empty ranges past the last tile), reads K(j) and
-// V(j-1), then waits for all but its latest pair and meets the barrier.
 // Interleaved eight-wave schedule (fa_interleave.h): DMA pair j (K(j+2),
 // V(j+1)) is issued at the start of iteration j, before the barrier, so it
 // may run while slower waves are still in iteration j-1; after the barrier
@@ -709,47 +706,11 @@ static void check_il_schedule(int ntiles) {
   }
 }
 
-static void check_w2_schedule(int ntiles) {
-  const int NS = kStages;
-  int ktile[3] = {0, ntiles > 1 ? 1 : -1, -1}, vtile[3] = {0, -1, -1};
-  // slot (iteration) after which each stage's latest DMA is waited for
-  int kland[3] = {-1, -1, -1}, vland[3] = {-1, -1, -1};
-  int kread_last[3] = {-1, -1, -1}, vread_last[3] = {-1, -1, -1};
-  int pend_k = -1, pend_v = -1;  // stages of the latest pair, not yet waited for
-  for (int j = 0; j <= ntiles; ++j) {
-    // DMA pair j at the start of iteration j
-    const int sk = (j + 2) % NS, sv = (j + 1) % NS;
-    CHECK(kread_last[sk] < j, "K stage refilled while still read");
-    CHECK(vread_last[sv] < j, "V stage refilled while still read");
-    ktile[sk] = j + 2 < ntiles ? j + 2 : -1;
-    vtile[sv] = j + 1 < ntiles ? j + 1 : -1;
-    kland[sk] = 1 << 30;
-    vland[sv] = 1 << 30;
-    // reads of iteration j
-    if (j < ntiles) {
-      CHECK(ktile[j % NS] == j && kland[j % NS] < j, "K(%d) not resident at iteration %d", j, j);
-      kread_last[j % NS] = j;
-    }
-    if (j >= 1) {
-      CHECK(vtile[(j + 2) % NS] == j - 1 && vland[(j + 2) % NS] < j,
-            "V(%d) not resident at iteration %d", j - 1, j);
-      vread_last[(j + 2) % NS] = j;
-    }
-    // end of iteration: everything but pair j has landed
-    if (pend_k >= 0) kland[pend_k] = j;
-    if (pend_v >= 0) vland[pend_v] = j;
-    pend_k = sk;
-    pend_v = sv;
-  }
-}
-
 int main() {
   check_lds<Cfg4<64>>();
   check_lds<Cfg4<128>>();
   check_lds<Cfg8<64>>();
   check_lds<Cfg8<128>>();
-  check_lds<CfgW2<64>>();
-  check_lds<CfgW2<128>>();
   check_tile_map();
   std::printf("work-group map: every head-group size: checked\n");
   // persistent work-groups: every item exactly once, ids rising per group
@@ -778,8 +739,6 @@ int main() {
       for (int id = 0; id < total; ++id) CHECK(cnt[id] == 1, "persistent item %d run %d times", id, cnt[id]);
     }
   std::printf("persistent work-group order: checked\n");
-  for (int ntiles = 1; ntiles <= 40; ++ntiles) check_w2_schedule(ntiles);
-  std::printf("two-block schedule: ntiles 1..40: checked\n");
   for (int ntiles = 1; ntiles <= 12; ++ntiles)
     for (int nw = 0; nw <= ntiles; ++nw)
       for (int one = 0; one < 2; ++one) check_pingpong(ntiles, nw, one != 0);
@@ -794,15 +753,11 @@ int main() {
       check_global<Cfg4<128>>(s[0], s[1], s[2], causal);
       check_global<Cfg8<64>>(s[0], s[1], s[2], causal);
       check_global<Cfg8<128>>(s[0], s[1], s[2], causal);
-      check_global<CfgW2<64>>(s[0], s[1], s[2], causal);
-      check_global<CfgW2<128>>(s[0], s[1], s[2], causal);
     }
   check_lengths<Cfg4<64>>();
   check_lengths<Cfg4<128>>();
   check_lengths<Cfg8<64>>();
   check_lengths<Cfg8<128>>();
-  check_lengths<CfgW2<64>>();
-  check_lengths<CfgW2<128>>();
   std::printf("query/key length pairs (bottom-right causal), padded rows: checked\n");
   // full-size shapes (O coverage tracked up to 64M elements)
   check_global<Cfg4<64>>(1, 16, 1024, true);
@@ -811,22 +766,9 @@ int main() {
   check_global<Cfg8<128>>(1, 8, 16384, true);
   check_global<Cfg4<128>>(1, 1, 65536, true);
   check_global<Cfg8<128>>(1, 1, 65536, true);
-  check_global<CfgW2<128>>(2, 16, 8192, true);
-  check_global<CfgW2<64>>(10, 64, 1024, false);
-  check_global<CfgW2<128>>(1, 1, 65536, true);
-  // interleaved eight-wave kernel (16-bit)
-  check_lds<CfgIL<64>>();
-  check_lds<CfgIL<128>>();
+  // interleaved eight-wave work-group (the 8-bit kernel's body)
   for (int ntiles = 1; ntiles <= 40; ++ntiles) check_il_schedule(ntiles);
   std::printf("interleaved schedule: ntiles 1..40: checked\n");
-  for (auto& s : shapes)
-    for (int causal = 0; causal < 2; ++causal) {
-      check_global<CfgIL<64>>(s[0], s[1], s[2], causal);
-      check_global<CfgIL<128>>(s[0], s[1], s[2], causal);
-    }
-  check_lengths<CfgIL<64>>();
-  check_lengths<CfgIL<128>>();
-  check_global<CfgIL<128>>(2, 16, 8192, true);
   // 8-bit kernels (ping-pong with 128-key tiles, interleaved with 64-key tiles)
   check_lds8<CfgF8>();
   check_lds8<CfgF8i>();

@@ -7,56 +7,80 @@ import subprocess
 
 import pytest
 
+import diag
 import exact_attention_16_amd as fa
 from exact_attention_16_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+DIAG_HEADER = os.path.join(ROOT, "include", "fa_fwd_diag.h")
 
 OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG, LAYOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M))
 
 
+def _exported(path):
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("no nm")
+    out = subprocess.run([nm, "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return set(re.findall(r" T (fa_\w+)$", out, flags=re.M))
+
+
 def test_header_declares_the_entry_points():
-    assert _declared() == {"fa_fwd", "fa_fwd_f16", "fa_fwd_bf16", "fa_fwd_diag",
-                           "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_kt", "fa_fwd_fp8",
-                           "fa_fwd_tile", "fa_strerror", "fa_version"}
+    assert _declared() == {"fa_fwd", "fa_fwd_f16", "fa_fwd_bf16", "fa_fwd_strided",
+                           "fa_fwd_varlen", "fa_fwd_kt", "fa_fwd_fp8", "fa_fwd_tile",
+                           "fa_strerror", "fa_version"}
+    assert _declared(DIAG_HEADER) == {"fa_fwd_diag"}
 
 
 def test_library_exports_every_declared_symbol():
+    """The product library exports exactly the product header's entry points
+    (no diagnostic hook); the diagnostic library exactly its own."""
     lib = fa.load()
     for name in _declared():
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
-    nm = shutil.which("nm")
-    if nm:
-        out = subprocess.run([nm, "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
-                             text=True, check=True).stdout
-        exported = set(re.findall(r" T (fa_\w+)$", out, flags=re.M))
-        assert exported == _declared()
+    assert _exported(fa.LIB_PATH) == _declared()
+    dlib = diag.load_diag()
+    for name in _declared(DIAG_HEADER):
+        assert hasattr(dlib, name), name
+        assert name in diag.SIGNATURES, name
+    assert _exported(diag.DIAG_PATH) == _declared(DIAG_HEADER)
 
 
-def test_kernel_launch_stubs_are_defined():
-    """Every kernel instantiation the launcher references has a host stub."""
+def _stubs(path):
     nm = shutil.which("nm")
     if nm is None:
         pytest.skip("no nm")
-    out = subprocess.run([nm, "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
-    stubs = [l for l in out.splitlines() if "device_stub" in l]
-    # 5 kernels x 2 dtypes x 2 head dims x 2 masks x 3 (production, two diagnostic
-    # thresholds), the transposed-K kernel x 2 dtypes x 2 head dims x 2 masks,
-    # and the 8-bit kernel x 2 head dims x 2 masks
-    assert len(stubs) == 132
+    out = subprocess.run([nm, "-D", path], capture_output=True, text=True, check=True).stdout
+    return [l for l in out.splitlines() if "device_stub" in l]
+
+
+def test_kernel_launch_stubs_are_defined():
+    """Every kernel instantiation the launchers reference has a host stub."""
+    stubs = _stubs(fa.LIB_PATH)
+    # product: 2 kernels (ping-pong, four-wave) x 2 dtypes x 2 head dims x 2
+    # masks, the transposed-K kernel x 2 x 2 x 2, the 8-bit kernel x 2 x 2
+    assert len(stubs) == 28
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
+    assert not [l for l in stubs if "ELb1EEEv" in l and "fa_fwd_pp_kt" not in l
+                and "fa_fwd_il8" not in l], "instrumented kernels in the product library"
+    dstubs = _stubs(diag.DIAG_PATH)
+    # diagnostic: 3 kernels (four-wave, ping-pong, persistent) x 2 dtypes x 2
+    # head dims x 2 masks x 2 lag thresholds
+    assert len(dstubs) == 48
+    assert not [l for l in dstubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 310
+    assert fa.fa_version() == 400
     for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG, LAYOUT):
         assert fa.fa_strerror(st) and fa.fa_strerror(st) != "unknown status"
     assert fa.fa_strerror(12345) == "unknown status"
@@ -126,14 +150,17 @@ def test_diag_validation():
     a = GOOD
     args = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 8, 64, 0, 0.1, None, 0)
     ev = 0x20000000000
-    assert fa.fa_fwd_diag(*args, 3, 0, ev, check=False) == ARG
-    assert fa.fa_fwd_diag(*args, 8, 6, ev, check=False) == ARG
-    assert fa.fa_fwd_diag(*args, 8, -1, ev, check=False) == ARG
-    assert fa.fa_fwd_diag(*args, 8, 0, 0, check=False) == NULL
-    assert fa.fa_fwd_diag(*args, 0, 2, ev + 4, check=False) == ALIGN
+    assert diag.fa_fwd_diag(*args, 3, 0, ev, check=False) == ARG
+    for retired in (3, 4, 6, -1):
+        assert diag.fa_fwd_diag(*args, 8, retired, ev, check=False) == ARG
+    assert diag.fa_fwd_diag(*args, 8, 0, 0, check=False) == NULL
+    assert diag.fa_fwd_diag(*args, 0, 2, ev + 4, check=False) == ALIGN
+    # the product checks run first
+    bad = (a["q"], a["k"], a["v"], a["q"], a["lse"], 1, 1, 8, 64, 0, 0.1, None, 0)
+    assert diag.fa_fwd_diag(*bad, 8, 0, ev, check=False) == ALIAS
     e = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 0, 64, 0, 0.1, None, 0)
-    for variant in (0, 1, 2, 3, 4, 5):
-        assert fa.fa_fwd_diag(*e, 8, variant, ev, check=False) == OK
+    for variant in (0, 1, 2, 5):
+        assert diag.fa_fwd_diag(*e, 8, variant, ev, check=False) == OK
 
 
 def test_error_raises_with_name():
@@ -194,6 +221,10 @@ def _with(i, x):
     (_with(2, 68), {}, ALIGN),              # q rows not 16-byte aligned
     (_with(7, 64 * 3 + 4), {}, ALIGN),      # v heads not 16-byte aligned
     (_with(11, 1 << 24), {}, DIM),          # 32-bit offsets within one head
+    (_with(1, 1 << 62), {}, DIM),           # q head stride: (H-1)*stride overflows 64 bits
+    (_with(0, (1 << 62) + 8), {}, DIM),     # q batch stride likewise
+    (_with(10, 1 << 41), {}, DIM),          # above the 2^40 stride cap
+    (_with(13, 1 << 62), {}, DIM),          # lse head stride
     (None, dict(o=K + 4096), ALIAS),        # o inside k's span
     (None, dict(lse=O + 64), ALIAS),
 ])
@@ -320,6 +351,56 @@ def test_torch_helpers_reject_host_tensors_before_any_launch():
         fa.attention_varlen(q[0, 0][:, None, :], q[0, 0][:, None, :], q[0, 0][:, None, :],
                             torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                             8, 8, True)
+
+
+@pytest.mark.parametrize("bad,match", [
+    (dict(out_dtype="float32"), "out must be"),       # 4-byte elements into a 2-byte output
+    (dict(out_shape=(1, 2, 7, 64)), "out must have shape"),
+    (dict(lse_dtype="float16"), "lse must be float32"),  # 4-byte stores into 2-byte lse
+    (dict(lse_shape=(1, 2, 4)), "lse must have shape"),
+])
+def test_torch_helpers_check_out_and_lse_before_any_launch(bad, match):
+    """A caller-supplied out or lse of the wrong type or shape would be
+    written past its end by the kernel (the C side sees only pointers):
+    the helpers refuse it first."""
+    import torch
+    dt = {"float32": torch.float32, "float16": torch.float16}
+    q = torch.zeros((1, 2, 8, 64), dtype=torch.float16)
+    out = torch.zeros(bad.get("out_shape", (1, 2, 8, 64)), dtype=dt[bad.get("out_dtype", "float16")])
+    lse = torch.zeros(bad.get("lse_shape", (1, 2, 8)), dtype=dt[bad.get("lse_dtype", "float32")])
+    with pytest.raises(ValueError, match=match):
+        fa.attention(q, q, q, True, out=out, lse=lse)
+    with pytest.raises(ValueError, match=match):
+        fa.attention(q, q, q, True, out=out, lse=lse, layout="bhsd")
+    with pytest.raises(ValueError, match=match):
+        fa.attention_kt(q, q.transpose(-1, -2).contiguous(), q, True, out=out, lse=lse)
+    # varlen: q [total, H, D], out the same, lse [H, total]
+    qv = torch.zeros((8, 2, 64), dtype=torch.float16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    out_v = torch.zeros(bad.get("out_shape", (8, 2, 64))[-3:] if "out_shape" in bad else (8, 2, 64),
+                        dtype=dt[bad.get("out_dtype", "float16")])
+    lse_v = torch.zeros((2, 8) if "lse_shape" not in bad else (2, 4),
+                        dtype=dt[bad.get("lse_dtype", "float32")])
+    if "out_shape" in bad:
+        out_v = torch.zeros((7, 2, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match=match):
+        fa.attention_varlen(qv, qv, qv, cu, cu, 8, 8, True, out=out_v, lse=lse_v)
+    # 8-bit: out must be bf16
+    q8 = torch.zeros((1, 2, 8, 64), dtype=torch.uint8)
+    out8 = torch.zeros(bad.get("out_shape", (1, 2, 8, 64)),
+                       dtype=torch.float32 if "out_dtype" in bad else torch.bfloat16)
+    with pytest.raises(ValueError, match=match):
+        fa.attention_fp8(q8, q8, q8, 1.0, 1.0, 1.0, True, out=out8, lse=lse)
+
+
+def test_torch_helpers_check_the_device_of_out():
+    """out on another device than q (a host buffer for a device q) is refused.
+    Without a GPU, q itself is on the host, so a meta-device out stands in."""
+    import torch
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.float16)
+    out = torch.empty((1, 1, 8, 64), dtype=torch.float16, device="meta")
+    with pytest.raises(ValueError, match="out must be on"):
+        fa.attention(q, q, q, True, out=out)
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):

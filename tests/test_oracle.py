@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import oracle.attention as OA
+import oracle.online as OO
 import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -220,6 +221,91 @@ def test_online_threshold_reduces_rescales():
     eager = oracle.online_softmax_attention(q, k, v, True, 0.2, 64, 0.0)["rescales"].sum()
     lazy = oracle.online_softmax_attention(q, k, v, True, 0.2, 64, 8.0)["rescales"].sum()
     assert eager > 0 and lazy < eager / 10
+
+
+def _rescale_golden():
+    with open(os.path.join(GOLDEN, "rescale_counts.json")) as f:
+        return json.load(f)
+
+
+def _run_rescale_case(case, block_n):
+    keys = np.array([x for t in case["tiles"] for x in t], dtype=np.float64)
+    S = len(keys)
+    q = np.ones((S, 1))
+    k = keys[:, None]
+    v = np.arange(S, dtype=np.float64)[:, None]
+    return oracle.online_softmax_attention(q, k, v, False, math.log(2.0), block_n=block_n,
+                                           threshold_log2=case["threshold_log2"])
+
+
+def _rescale_golden_passes():
+    g = _rescale_golden()
+    assert math.log(2.0) * OO.LOG2E == 1.0  # the fixture's premise: ScaleLog2 is exactly 1
+    for case in g["cases"]:
+        r = _run_rescale_case(case, g["block_n"])
+        if not (np.all(r["rescales"] == case["rescales_per_row"])
+                and r["max_p"] == case["max_p"] and r["min_history"] == case["min_history"]):
+            return False
+    return True
+
+
+def test_rescale_counts_match_the_hand_counted_cases():
+    """The float64 model's rebase count is what the GPU's event counter is
+    compared with; here it is pinned to cases counted by hand from the rule."""
+    g = _rescale_golden()
+    assert math.log(2.0) * OO.LOG2E == 1.0
+    for case in g["cases"]:
+        r = _run_rescale_case(case, g["block_n"])
+        assert np.all(r["rescales"] == case["rescales_per_row"]), case["name"]
+        assert r["max_p"] == case["max_p"], case["name"]
+        assert r["min_history"] == case["min_history"], case["name"]
+        # the result is still exact attention (the base cancels)
+        keys = np.array([x for t in case["tiles"] for x in t])
+        w = np.exp2(keys - keys.max())
+        np.testing.assert_allclose(r["o"][:, 0], (w @ np.arange(len(keys))) / w.sum(),
+                                   rtol=1e-12)
+
+
+def _rebase_ge(b, m, thr):  # rebases at exactly b + threshold
+    cand = np.maximum(b, m)
+    rebase = cand >= b + thr
+    with np.errstate(invalid="ignore"):
+        hist = np.where(rebase, np.exp2(b - cand), 1.0)
+    return np.where(rebase, cand, b), hist, rebase & np.isfinite(b)
+
+
+def _rebase_first_counted(b, m, thr):  # the first tile counted as a rescale
+    nb, hist, counted = _REBASE(b, m, thr)
+    return nb, hist, counted | ~np.isfinite(b)
+
+
+def _rebase_to_tile_max(b, m, thr):  # the base follows every tile's max, down as well
+    nb = np.where(np.isfinite(m), m, b)
+    with np.errstate(invalid="ignore"):
+        hist = np.where(nb != b, np.exp2(b - nb), 1.0)
+    return nb, hist, (nb != b) & np.isfinite(b)
+
+
+def _rebase_history_inverted(b, m, thr):
+    nb, hist, counted = _REBASE(b, m, thr)
+    with np.errstate(divide="ignore"):
+        return nb, np.where(counted, 1.0 / hist, hist), counted
+
+
+_REBASE = OO._rebase
+_REBASE_MUTANTS = {"rebase at exactly b + 8": _rebase_ge,
+                   "first tile counted": _rebase_first_counted,
+                   "base follows the tile max down": _rebase_to_tile_max,
+                   "history inverted": _rebase_history_inverted}
+
+
+@pytest.mark.parametrize("name", sorted(_REBASE_MUTANTS))
+def test_planted_rebase_mistake_is_caught(name, monkeypatch):
+    assert _rescale_golden_passes()
+    monkeypatch.setattr(OO, "_rebase", _REBASE_MUTANTS[name])
+    with np.errstate(all="ignore"):
+        caught = not _rescale_golden_passes()
+    assert caught, f"planted mistake not caught: {name}"
 
 
 # ------------------------------------------- planted mistakes must fail a pin

@@ -120,9 +120,11 @@ def test_rounding_p_stays_within_the_bound(case):
     # nearest rounding of the scaled probabilities
     o_near = (rne_e4m3(s * p) / s) @ v / l[:, None]
     assert (np.abs(o_near - o) <= bound * (1 + 1e-9) + 1e-15).all()
-    # a factor that differs per key (the kernel's base moves between key
-    # tiles), never below p_scale and never taking a value above 256
-    f = s * 2.0 ** np.random.default_rng(case[0]).integers(0, 3, size=p.shape[1])
+    # a factor that differs per key (the running base moves between key
+    # tiles): any power of two from p_scale up to the one that puts the
+    # row maximum (p = 1) at the top of the lagging base's range, 2^8
+    top = int(round(math.log2(F.P_MAX / s)))
+    f = s * 2.0 ** np.random.default_rng(case[0]).integers(0, top + 1, size=p.shape[1])
     o_var = (rne_e4m3(f * p) / f) @ v / l[:, None]
     assert (np.abs(o_var - o) <= bound * (1 + 1e-9) + 1e-15).all()
     # the worst any rounding to a neighbouring grid point within half a spacing
@@ -131,6 +133,38 @@ def test_rounding_p_stays_within_the_bound(case):
     assert (worst <= bound * (1 + 1e-9) + 1e-15).all()
     # and the bound is no more than twice that worst case
     assert (bound <= 2 * worst + 1e-15).all()
+
+
+@pytest.mark.parametrize("case", CASES[:4])
+def test_bound_covers_every_scale_in_the_lagging_range(case):
+    """The bound is taken at the least favourable factor the reading allows
+    (the row maximum at 1). Rounding after any larger power-of-two factor
+    that keeps the row maximum within 2^8 stays inside the same bound, so it
+    does not depend on which factor an implementation picks."""
+    q, k, v, scale = _case(*case[:5], std_q=case[5], dominant=case[6])
+    causal = case[4]
+    rows = np.arange(q.shape[0])
+    o, _ = oracle.attention_rows(q, k, v, rows, causal, scale)
+    bound = F.pv_rounding_bound(q, k, v, rows, causal, scale)
+    p, l = _probs(q, k, causal, scale)
+    for e in range(0, 9):
+        f = 2.0 ** e
+        assert (f * p).max() <= F.P_MAX
+        o_f = (rne_e4m3(f * p) / f) @ v / l[:, None]
+        assert (np.abs(o_f - o) <= bound * (1 + 1e-9) + 1e-15).all(), e
+    # and a bound taken at a larger factor is tighter: the factor matters to
+    # the bound only through the absolute term
+    tighter = F.pv_rounding_bound(q, k, v, rows, causal, scale, p_scale=64.0)
+    assert (tighter <= bound).all()
+
+
+def test_reading_constants():
+    """The reading's constants: E4M3 (3 mantissa bits, smallest normal 2^-6,
+    subnormal spacing 2^-9, largest 448) and V41's range (0, 2^8]."""
+    assert F.REL_HALF_ULP == 2.0 ** -4 and F.ABS_HALF_ULP == 2.0 ** -10
+    assert F.P_MAX == 2.0 ** 8 and F.P_MAX < 448 and F.P_SCALE == 1.0
+    # the largest finite E4M3 code decodes to 448
+    assert W.decode(np.array([0x7E], np.uint8), W.E4M3)[0] == 448.0
 
 
 def test_bound_needs_its_absolute_term(monkeypatch):

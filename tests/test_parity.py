@@ -13,8 +13,9 @@ import torch
 import exact_attention_16_amd as fa
 import oracle
 import workloads as W
-from gpu_util import (LSE_TOL, O_TOL, compare_rows, o_to_f64, run, sample_rows, to_dev,
-                      device)
+import diag
+from gpu_util import (LSE_TOL, O_TOL, compare_rows, max_abs_err, o_to_f64, run, sample_rows,
+                      to_dev, device)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,8 +24,8 @@ def _banner(msg):
     print(msg, flush=True)
 
 
-VARIANTS = {"k4": fa.VARIANT_FOUR_WAVE, "pp": fa.VARIANT_PING_PONG, "w2": fa.VARIANT_TWO_BLOCK,
-            "il": fa.VARIANT_INTERLEAVE, "ps": fa.VARIANT_PERSISTENT}
+VARIANTS = {"k4": diag.VARIANT_FOUR_WAVE, "pp": diag.VARIANT_PING_PONG,
+            "ps": diag.VARIANT_PERSISTENT}
 
 
 def _check_full(qb, kb, vb, dtype, causal, scale, tag, variant=None):
@@ -47,7 +48,7 @@ def test_tiny_workload(causal):
     _check_full(*W.make_inputs(w), w.dtype, causal, w.scale, f"tiny causal={causal}")
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
+@pytest.mark.parametrize("kernel", sorted(VARIANTS))
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
@@ -62,7 +63,7 @@ def test_small_shapes_all_rows(S, causal, D, dtype, kernel):
                 f"S={S} D={D} {dtype} causal={causal} kernel={kernel}", VARIANTS[kernel])
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
+@pytest.mark.parametrize("kernel", sorted(VARIANTS))
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_many_tiles_all_rows(causal, D, kernel):
@@ -82,7 +83,7 @@ def test_kernels_agree(D):
     S, dt = 777, W.F16
     qb, kb, vb = (W.random_bits((2, 2, S, D), dt, 3000 + D + i) for i in range(3))
     res = [_check_full(qb, kb, vb, dt, True, D ** -0.5, f"agree D={D} {k}", VARIANTS[k])
-           for k in ("k4", "pp", "w2", "il", "ps")]
+           for k in sorted(VARIANTS)]
     for other in res[1:]:
         assert np.abs(res[0][0] - other[0]).max() <= O_TOL[dt]
         assert np.abs(res[0][1] - other[1]).max() <= LSE_TOL
@@ -215,7 +216,7 @@ def _diag(qb, kb, vb, dtype, causal, scale, thr, variant=0):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device())
     ev = torch.zeros(1, dtype=torch.int64, device=device())
     B, H, S, D = q.shape
-    fa.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+    diag.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                    B, H, S, D, causal, scale, torch.cuda.current_stream().cuda_stream,
                    W.DTYPE_CODE[dtype], thr, variant, ev.data_ptr())
     torch.cuda.synchronize()
@@ -230,12 +231,12 @@ def test_persistent_equals_pingpong_full_size(name):
     w = W.WORKLOADS[name]
     _banner(f"persistent vs ping-pong, {name}: B={w.B} H={w.H} S={w.S} D={w.D}")
     qb, kb, vb = W.make_inputs(w)
-    o2, l2, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, fa.VARIANT_PING_PONG)
-    o5, l5, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, fa.VARIANT_PERSISTENT)
+    o2, l2, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, diag.VARIANT_PING_PONG)
+    o5, l5, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, diag.VARIANT_PERSISTENT)
     assert np.array_equal(o2, o5) and np.array_equal(l2, l5)
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
+@pytest.mark.parametrize("kernel", sorted(VARIANTS))
 @pytest.mark.parametrize("D", [64, 128])
 def test_lagging_and_eager_rescale_both_match(D, kernel):
     """Threshold 8 (production) and 0 (eager) both meet tolerance on a steep
@@ -262,7 +263,7 @@ def test_lagging_and_eager_rescale_both_match(D, kernel):
     # the float64 model of the algorithm, same KV tile size
     # KV tile of the forced kernel: the eight-wave kernel's from the tile
     # query on a grid large enough for fa_fwd to pick it
-    bn = {"k4": 64, "pp": fa.fa_fwd_tile(D, 1, 256, 1024)[1], "w2": 32, "il": 64,
+    bn = {"k4": 64, "pp": fa.fa_fwd_tile(D, 1, 256, 1024)[1],
           "ps": fa.fa_fwd_tile(D, 1, 256, 1024)[1]}[kernel]
     model = {8: 0, 0: 0}
     for h in range(w.H):
@@ -276,6 +277,32 @@ def test_lagging_and_eager_rescale_both_match(D, kernel):
         assert abs(gpu - model[thr]) <= max(4, 0.02 * model[thr]), (thr, gpu, model[thr])
 
 
+@pytest.mark.parametrize("h", [0, 3])
+def test_ramp_workload_fires_the_lagging_rescale(h):
+    """The rescale-stress workload (B=1, H=8, S=16384, D=128, bf16, causal,
+    key ramp) exists to exercise the lagging base. On two of its heads the
+    production kernel at threshold 8 must rebase (events > 0) as often as the
+    float64 model of the same algorithm with the same KV tile predicts, and
+    still match the oracle."""
+    w = W.WORKLOADS["ramp"]
+    _banner(f"ramp head {h}: S={w.S} D={w.D}, threshold 8, ping-pong kernel")
+    qb, kb, vb = W.make_inputs(w)
+    q1, k1, v1 = (np.ascontiguousarray(x[:, h:h + 1]) for x in (qb, kb, vb))
+    og, lg, ev = _diag(q1, k1, v1, w.dtype, True, w.scale, 8, diag.VARIANT_PING_PONG)
+    bn = fa.fa_fwd_tile(w.D, 1, 256, 1024)[1]  # the ping-pong kernel's KV tile
+    q, k, v = (W.decode(x[0, h], w.dtype) for x in (qb, kb, vb))
+    model = oracle.online_softmax_attention(q, k, v, True, float(np.float32(w.scale)),
+                                            block_n=bn, threshold_log2=8)
+    expected = int(model["rescales"].sum())
+    _banner(f"ramp head {h}: GPU events={ev} model={expected}")
+    assert expected > 0 and ev > 0
+    assert abs(ev - expected) <= max(4, 0.02 * expected), (ev, expected)
+    eo, el = compare_rows(q1, k1, v1, w.dtype, True, w.scale, og, lg,
+                          [((0, 0), sample_rows(w.S, 64, seed=h))])
+    _banner(f"ramp head {h}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= O_TOL[w.dtype] and el <= LSE_TOL
+
+
 # ---------------------------------------------------- hygiene of the launch
 
 def test_deterministic():
@@ -286,7 +313,7 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("kernel", ["k4", "pp", "w2", "il", "ps"])
+@pytest.mark.parametrize("kernel", sorted(VARIANTS))
 @pytest.mark.parametrize("D", [64, 128])
 def test_no_writes_outside_outputs(D, kernel):
     """Outputs embedded in guard bands: the kernel writes only O and lse."""
@@ -299,7 +326,7 @@ def test_no_writes_outside_outputs(D, kernel):
     o = obuf[g:g + n]
     lse = lbuf[g:g + nl]
     ev = torch.zeros(1, dtype=torch.int64, device=device())
-    fa.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+    diag.fa_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
                    S, D, 1, D ** -0.5, torch.cuda.current_stream().cuda_stream, fa.FA_F16, 8,
                    VARIANTS[kernel], ev.data_ptr())
     torch.cuda.synchronize()

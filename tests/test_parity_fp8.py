@@ -21,7 +21,7 @@ import exact_attention_16_amd as fa
 import oracle
 import oracle.fp8 as F
 import workloads as W
-from gpu_util import LSE_TOL, device, sample_rows
+from gpu_util import LSE_TOL, device, max_abs_err, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def _check_head(codes, ds, o_gpu, lse_gpu, b, h, rows, causal, scale, tag):
     assert np.isfinite(og).all(), tag
     err = np.abs(og - o_ref)
     ratio = float((err / tol).max())
-    el = float(np.abs(lse_gpu[b, h, rows] - l_ref).max())
+    el = max_abs_err(lse_gpu[b, h, rows], l_ref)
     return ratio, float(err.max()), el
 
 
