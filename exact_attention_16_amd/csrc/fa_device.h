@@ -65,8 +65,12 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // the compiler turns the select of a uniform condition into branches that
 // split the DMA issue into blocks of its own. The 8-bit kernel runs about 1%
 // faster this way; the 16-bit kernels' time is unchanged.
+// The count is wave-uniform (it comes from sizes and the tile index); the
+// readfirstlane says so to the compiler, which otherwise may derive it from a
+// lane-varying expression that shares terms with it (the mask's bound) and
+// then wraps every DMA issue in a loop over the lanes' values.
 __device__ __forceinline__ uint32_t dma_bytes(bool live, uint32_t bytes) {
-  return bytes * (uint32_t)live;
+  return __builtin_amdgcn_readfirstlane(bytes * (uint32_t)live);
 }
 
 // LDS pointers stay in address space 3 from the point where each shared

@@ -8,6 +8,7 @@
 #pragma once
 #include "fa_device.h"
 
+
 namespace fa {
 
 template <class W>
@@ -112,7 +113,10 @@ __device__ __forceinline__ void pp_item(const Problem& P, W& w, lds_char* const 
   w.dma_k(lk0, 0);
   w.dma_k(lk1, 1, ntiles);
   w.dma_v(lv0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
+  // Slot 0 reads only Q and K(0): K(1) and V(0), the last 2*DPW loads, may
+  // still be in flight. They are first read in slot 1, after the end-of-slot
+  // wait for all but the latest DMA pair.
+  wait_vm_lgkm0<2 * DPW>();
   wg_barrier();
 
   // With two barriers per step group A runs step j in slots (2j, 2j+1),

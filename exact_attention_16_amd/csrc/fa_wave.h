@@ -11,6 +11,7 @@
 
 #include "fa_device.h"
 
+
 namespace fa {
 
 template <typename T> struct Ops;
@@ -189,20 +190,28 @@ struct Wave : RowState<C, CAUSAL, THR> {
     if constexpr (KT) read_ahead<8, NDC * NKB, 2>();
     else read_ahead<4, NDC * NKB, 1>();
   }
+  // Hides the keys of the tile at kv0 this lane's row cannot see: keys past
+  // Lk and, causal, past qrow + off. Element (kb, r) holds key
+  // kv0 + 8*hh + 32*kb + 16*(r/8) + r%8 (acc_key32), a lane base plus a
+  // compile-time offset, so one bound on the offset covers both conditions:
+  // one compare and one select per score.
   __device__ __forceinline__ void mask(f32x16 (&s)[NKB], int kv0) const {
+    const int base = kv0 + 8 * hh;
+    int lim = Lk - base;
+    if (CAUSAL) lim = min(lim, qrow + off + 1 - base);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * kb + acc_key32(r, hh);
-        const bool vis = key < Lk && (!CAUSAL || key <= qrow + off);
-        s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        const int o = 32 * kb + acc_key32(r, 0);
+        s[kb][r] = o < lim ? s[kb][r] : -INFINITY;
       }
   }
-  // p = 2^(s*c - b), row sum of the unrounded p, P packed for the P.V MFMA
-  __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[NKB], u32x4 (&p)[NKC]) {
+  // p = 2^(s*c - b) and P packed for the P.V MFMA; returns this lane's sum of
+  // the unrounded p over the tile (its k-half of each row's keys)
+  __device__ __forceinline__ float exp_tile(const f32x16 (&s)[NKB], u32x4 (&p)[NKC]) const {
     const float nb = (b == -INFINITY) ? 0.f : -b;  // fully hidden row: p = 0
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four sum chains, so no add waits on the one before
+    float ls[4];  // four sum chains, so no add waits on the one before
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -211,12 +220,17 @@ struct Wave : RowState<C, CAUSAL, THR> {
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           e[x] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * g + x], c, nb));
+          if (kb == 0 && g == 0 && x < 4) ls[x] = 0.f;
           ls[x & 3] += e[x];
         }
         p[2 * kb + g] = (u32x4){Ops<T>::pack2(e[0], e[1]), Ops<T>::pack2(e[2], e[3]),
                                 Ops<T>::pack2(e[4], e[5]), Ops<T>::pack2(e[6], e[7])};
       }
-    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  }
+  // p = 2^(s*c - b), row sum of the unrounded p, P packed for the P.V MFMA
+  __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[NKB], u32x4 (&p)[NKC]) {
+    lsum += exp_tile(s, p);
   }
   // rare path: some row of the wave moved its base -> rescale O
   __device__ __forceinline__ void rescale(int j, float hist) {
@@ -226,13 +240,62 @@ struct Wave : RowState<C, CAUSAL, THR> {
       for (int jd = 0; jd < NDB; ++jd) o[jd] *= hist;
     }
   }
-  // softmax of tile j in place: mask, base update, rescale of O, P(j)
+  // Softmax of tile j in place: mask, base update, rescale of O, P(j).
+  // On a row's first tile the base comes from the tile max (from -inf; V41
+  // steps 2-4). After that the exponentials come first, against the current
+  // base and in place of the scores: every p of a lane is at most that lane's
+  // share of the tile sum, so when no share exceeds 2^THR no scaled score
+  // exceeds b + THR and the base stays with history 1 (V41 step 4), and the
+  // tile's max is never formed. Otherwise (rare) the row max of the p gives
+  // the candidate b + log2(max p); a row whose max p exceeds 2^THR moves its
+  // base there and scales its p, its row sum and O by 2^(b_old - b_new).
+  // A row's visible keys are a prefix from key 0, so a row whose base is
+  // still -inf after its first tile sees no key: all its p are 0 (base 0).
   __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NKB], u32x4 (&p)[NKC], int j) {
     const int kv0 = j * BN;
     if (this->needs_mask(kv0)) mask(s, kv0);
-    const float hist = this->softmax_max(s);
+    float hist = 1.f;
+    if (j == 0) hist = this->softmax_max(s);
+    const float nb = (b == -INFINITY) ? 0.f : -b;
+    float ls[4];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, nb));
+        if (kb == 0 && r < 4) ls[r] = 0.f;
+        ls[r & 3] += s[kb][r];
+      }
+    float ts = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    if (j >= 1 && __builtin_amdgcn_ballot_w64(!(ts <= (float)(1 << THR))) != 0) {
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
+      mx = max_xor32(mx);
+      const bool rebase = mx > (float)(1 << THR);
+      if (__builtin_amdgcn_ballot_w64(rebase) != 0) {
+        const float lm = rebase ? __builtin_amdgcn_logf(mx) : 0.f;  // log2 of the row's max p
+        hist = rebase ? __builtin_amdgcn_exp2f(-lm) : 1.f;
+        b += lm;
+        lsum *= hist;
+        ts *= hist;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] *= hist;
+      }
+    }
     rescale(j, hist);
-    softmax_exp(s, p);
+    lsum += ts;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const f32x16& e = s[kb];
+        const int r0 = 8 * g;
+        p[2 * kb + g] = (u32x4){Ops<T>::pack2(e[r0 + 0], e[r0 + 1]), Ops<T>::pack2(e[r0 + 2], e[r0 + 3]),
+                                Ops<T>::pack2(e[r0 + 4], e[r0 + 5]), Ops<T>::pack2(e[r0 + 6], e[r0 + 7])};
+      }
   }
 
   // normalise once, write O and lse (rows past Lq dropped by the range

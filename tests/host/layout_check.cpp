@@ -619,13 +619,17 @@ static void check_pingpong(int ntiles, int nw, bool one_barrier) {
     issue(g, &vst[(i + 1) % NS], i + 1 < ntiles ? i + 1 : -1, slot, i);
   };
 
-  // prologue (both groups, waited with vmcnt(0) before the first barrier);
-  // K stage 2 and V stages 1, 2 are first written by DMA pairs 0 and 1
+  // prologue (both groups): K(0), then K(1) and V(0); before the first
+  // barrier each group waits for all but its last 2*DPW loads, so K(0) has
+  // landed and K(1), V(0) (a pair of their own, id -1) are in flight until the
+  // first wait for all but the latest pair. K stage 2 and V stages 1, 2 are
+  // first written by DMA pairs 0 and 1.
   for (int g = 0; g < 2; ++g) {
-    issue(g, &kst[0], 0, -1, -1);
+    issue(g, &kst[0], 0, -1, -2);
+    wait_all(g, -1);
+    last_pair[g] = -1;
     issue(g, &kst[1], ntiles > 1 ? 1 : -1, -1, -1);
     issue(g, &vst[0], 0, -1, -1);
-    wait_all(g, -1);
   }
   auto step_reads = [&](int j, int t) {
     if (j >= 1 && j - 1 < nw) read(&vst[(j + 2) % NS], j - 1, t);
