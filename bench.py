@@ -22,6 +22,15 @@ values).
 16 causal sequences with seeded lengths in [256, 8192] (H=16, D=128, bf16),
 and prints its own JSON line; FLOPs then sum the metric over the sequences.
 
+Before the W warm-up steps the same call runs back to back for --settle-s
+seconds (default 0.3): the MI355X power manager needs tens of milliseconds
+of a given load to settle the engine clock, and the metric is sustained
+throughput. The engine clock is sampled (sysfs pp_dpm_sclk) during the timed
+region and reported with the fraction of the peak re-derived at that clock
+("sclk", "pct_of_peak_at_sclk"). Workloads under 64 MiB (tiny, dec) also get
+a cold-cache leg ("cold"): launches timed one by one after a 512 MiB scrub
+write that evicts L2 and the MALL.
+
 Extra modes (used to take profiles): --calibrate-copy runs plain device
 copies of a known size first (for scaling HBM byte counters);
 --no-cpu-baseline skips the oracle leg; --write-traffic FETCH_CSV WRITE_CSV
@@ -311,7 +320,8 @@ def main(argv=None) -> int:
                          "for workloads under 64 MiB)")
     ap.add_argument("--no-cold", dest="cold", action="store_false")
     ap.add_argument("--settle-s", type=float, default=0.3,
-                    help="seconds of plain device fills before the warm-up steps (0: none)")
+                    help="seconds of back-to-back calls before the warm-up steps, to bring the "
+                         "engine clock to its steady state under this load (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run plain 1 GiB device copies first (counter scaling)")
     ap.add_argument("--varlen", action="store_true",
@@ -354,7 +364,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     if args.calibrate_copy:
         calibrate_copy(torch, dev, stream)
-    settled = settle(torch, dev, stream, args.settle_s)
+    settled = settle(step, torch, args.settle_s)
 
     ms_per_step, wall, med_ms, clk = timed(step, stream, torch, args.steps, args.warmup)
     gpu_ms = ms_per_step * args.steps
@@ -482,28 +492,27 @@ def cold_timing(step, stream, torch, dev, alg_bytes: int, reps: int = 20) -> dic
             "note": "each launch alone after a 512 MiB scrub write (L2 and MALL evicted)"}
 
 
-def settle(torch, dev, stream, seconds: float) -> dict:
-    """Brings the GPU out of idle before the warm-up steps: plain device
-    fills of a 256 MiB buffer for `seconds`. From idle the power manager takes
-    tens of milliseconds of sustained load to raise the engine clock (the
-    first launches of the long workload after idle run at 1.7x their steady
-    duration), so without this a short warm-up leaves the clock ramp inside
-    the timed steps. The fills are not the attention kernel: the warm-up and
-    timed steps stay exactly W and K launches of it."""
+def settle(step, torch, seconds: float) -> dict:
+    """Brings the GPU to the steady state of this workload before the W
+    warm-up steps: the same call, back to back, for `seconds`. From idle, or
+    after lighter work, the power manager takes tens of milliseconds of this
+    load to settle the engine clock (the first launches of the long workload
+    after idle run up to 1.7x their steady duration, and still about 3%
+    slower after other work), and the metric is sustained throughput. These
+    launches are neither warm-up nor timed steps: those stay exactly W and
+    K."""
     if seconds <= 0:
-        return {"seconds": 0.0, "fills": 0}
-    buf = torch.empty(1 << 26, dtype=torch.float32, device=dev)
+        return {"seconds": 0.0, "launches": 0}
     n = 0
     t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        while time.perf_counter() - t0 < seconds:
-            for _ in range(8):
-                buf.fill_(float(n))
-                n += 1
-            stream.synchronize()
-    del buf
-    return {"seconds": round(time.perf_counter() - t0, 3), "fills": n,
-            "what": "256 MiB device fills before the warm-up steps (engine clock out of idle)"}
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            step()
+        n += 16
+        torch.cuda.synchronize()
+    return {"seconds": round(time.perf_counter() - t0, 3), "launches": n,
+            "what": "the same call, back to back, before the warm-up steps (engine clock to "
+                    "its steady state under this load)"}
 
 
 def bench_fp8(args, torch, fa, w) -> int:
@@ -524,7 +533,7 @@ def bench_fp8(args, torch, fa, w) -> int:
     torch.cuda.synchronize()
     if args.calibrate_copy:
         calibrate_copy(torch, dev, stream)
-    settled = settle(torch, dev, stream, args.settle_s)
+    settled = settle(step, torch, args.settle_s)
     ms, wall, med, clk = timed(step, stream, torch, args.steps, args.warmup)
     assert bool(torch.isfinite(lse).all()), "non-finite output"
     tflops = w.flops / (ms * 1e-3) / 1e12
@@ -584,7 +593,7 @@ def bench_varlen(args, torch, fa) -> int:
                          total, total, w.D, int(w.causal), w.scale, stream.cuda_stream,
                          W.DTYPE_CODE[w.dtype], st)
 
-    settled = settle(torch, dev, stream, args.settle_s)
+    settled = settle(step, torch, args.settle_s)
     ms, wall, med, clk = timed(step, stream, torch, args.steps, args.warmup)
     assert bool(torch.isfinite(lse).all()), "non-finite output"
     tflops = w.flops() / (ms * 1e-3) / 1e12

@@ -9,6 +9,7 @@
 #include "fa_device.h"
 
 
+
 namespace fa {
 
 template <class W>
