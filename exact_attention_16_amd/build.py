@@ -48,14 +48,31 @@ def compile_flags() -> list[str]:
     ]
 
 
-def _command(srcs, out, save_temps, resource_usage):
-    cmd = [hipcc(), *compile_flags(), *srcs, "-o", out + ".tmp"]
-    if resource_usage:
-        cmd += ["-Rpass-analysis=kernel-resource-usage"]
+def _command(srcs, out, save_temps):
+    # the resource-usage remarks are always on: scratch_use() checks them
+    cmd = [hipcc(), *compile_flags(), *srcs, "-o", out + ".tmp",
+           "-Rpass-analysis=kernel-resource-usage"]
     if save_temps:
         cmd += ["-save-temps=obj"]
         cmd[cmd.index("-o") + 1] = os.path.abspath(out + ".tmp")
     return cmd
+
+
+def scratch_use(remarks: str) -> list[tuple[str, int]]:
+    """Kernels whose resource-usage remarks report scratch memory (register
+    spills), with the bytes per lane. No kernel here may spill: besides the
+    cost, the stream form of the ping-pong kernel counts its vector-memory
+    instructions exactly in its waits, and spill loads and stores would make
+    those waits too short."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:", 1)[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            n = int(line.split("ScratchSize [bytes/lane]:", 1)[1].split()[0])
+            if n > 0:
+                out.append((name, n))
+    return out
 
 
 def build(verbose: bool = False, save_temps: str | None = None, resource_usage: bool = False,
@@ -67,7 +84,7 @@ def build(verbose: bool = False, save_temps: str | None = None, resource_usage: 
         os.makedirs(save_temps, exist_ok=True)
     procs = []
     for srcs, out in jobs:
-        cmd = _command(srcs, out, save_temps, resource_usage)
+        cmd = _command(srcs, out, save_temps)
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((out, subprocess.Popen(cmd, cwd=save_temps or None, stdout=subprocess.PIPE,
@@ -82,6 +99,12 @@ def build(verbose: bool = False, save_temps: str | None = None, resource_usage: 
             continue
         if verbose or resource_usage:
             print(text, flush=True)
+        spills = scratch_use(text)
+        if spills:
+            os.remove(out + ".tmp")
+            failed.append(f"{os.path.basename(out)}: kernels use scratch memory: "
+                          + ", ".join(f"{n} ({b} bytes/lane)" for n, b in spills))
+            continue
         os.replace(out + ".tmp", out)
     if failed:
         raise RuntimeError("\n".join(failed))

@@ -57,8 +57,20 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // Raw buffer descriptor over `bytes` bytes at `base`. A macro rather than a
 // function: a function or lambda returning the descriptor type makes the
 // host compilation pass drop the kernel launch stubs.
-#define FA_RSRC(base, bytes) \
-  __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>((const void*)(base)), 0, (int)(bytes), kBufferWord3)
+// Base and size are wave-uniform; they pass through readfirstlane so that
+// the descriptor is built in scalar registers even where the compiler has
+// kept them in vector registers (it would otherwise loop over the lanes'
+// values around every use). On values already scalar this costs nothing.
+#define FA_RSRC(base, bytes)                                                      \
+  __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>((const void*)fa::uniform_ptr(base)), 0, \
+                                    (int)__builtin_amdgcn_readfirstlane((uint32_t)(bytes)), \
+                                    kBufferWord3)
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
 
 // Byte count of a DMA source range: `bytes` when `live`, else 0 (an empty
 // range, which the DMA turns into zeros). A product rather than a select:
@@ -133,11 +145,19 @@ struct HeadRows {
   int Lq, Lk;
   long long q0, k0, v0, o0, l0;
 };
+// The offsets are read through the constant address space: they do not
+// change during a launch, so the reads are scalar loads of wave-uniform
+// values, also in code after the kernel's first stores (the persistent
+// form's later items), where a plain global read becomes a vector load whose
+// result the compiler treats as lane-varying.
+typedef __attribute__((address_space(4))) const int const_int;
 __device__ __forceinline__ HeadRows head_rows(const Problem& P, int bb, int h) {
   HeadRows r;
   if (P.cuq) {
-    const int sq = clampi(P.cuq[bb], 0, P.totq), eq = clampi(P.cuq[bb + 1], sq, P.totq);
-    const int sk = clampi(P.cuk[bb], 0, P.totk), ek = clampi(P.cuk[bb + 1], sk, P.totk);
+    const_int* cq = (const_int*)P.cuq;
+    const_int* ck = (const_int*)P.cuk;
+    const int sq = clampi(cq[bb], 0, P.totq), eq = clampi(cq[bb + 1], sq, P.totq);
+    const int sk = clampi(ck[bb], 0, P.totk), ek = clampi(ck[bb + 1], sk, P.totk);
     r.Lq = min(eq - sq, P.Sq);
     r.Lk = min(ek - sk, P.Sk);
     r.q0 = sq * P.qs + h * P.qh;

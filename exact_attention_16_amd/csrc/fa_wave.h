@@ -81,7 +81,7 @@ struct Wave : RowState<C, CAUSAL, THR> {
   uint32_t koff0, voff0, kdo0, vdo0;
   u32x4 qf[NDC];
   f32x16 o[NDB];
-  unsigned n_events;
+  unsigned n_events;  // rescale events of the wave's rows so far (wave-uniform)
 
   // Sets up this wave's rows of the work-group's query tile (see
   // RowState::locate); false when the tile lies wholly past its sequence's
@@ -234,7 +234,9 @@ struct Wave : RowState<C, CAUSAL, THR> {
   }
   // rare path: some row of the wave moved its base -> rescale O
   __device__ __forceinline__ void rescale(int j, float hist) {
-    if (DIAG && j >= 1 && hh == 0 && qrow < Lq && hist < 1.f) ++n_events;
+    if (DIAG && j >= 1)
+      n_events += (unsigned)__builtin_popcountll(
+          __builtin_amdgcn_ballot_w64(hh == 0 && qrow < Lq && hist < 1.f));
     if (j >= 1 && __builtin_amdgcn_ballot_w64(hist < 1.f) != 0) {
 #pragma unroll
       for (int jd = 0; jd < NDB; ++jd) o[jd] *= hist;
@@ -298,35 +300,47 @@ struct Wave : RowState<C, CAUSAL, THR> {
       }
   }
 
-  // normalise once, write O and lse (rows past Lq dropped by the range
-  // check). A row that sees no key (possible when Lk < Lq under the causal
-  // mask, or Lk = 0) gets O = 0 and lse = -inf.
-  __device__ __forceinline__ void epilogue(unsigned long long* events) {
+  // Normalise once, write O and lse. A row past Lq gets the byte offset
+  // where the range ends, so the range check drops it, also where its row
+  // times the row stride would wrap in 32 bits (a head's rows take less than
+  // 2^31 bytes, so no offset formed here wraps). Both k-halves of a row hold
+  // the same lse and both store it. A row that sees no key (possible when
+  // Lk < Lq under the causal mask, or Lk = 0) gets O = 0 and lse = -inf.
+  __device__ __forceinline__ void store_rows() {
     const float ltot = sum_xor32(lsum);
-    if (q0w < Lq) {
-      const auto ro = FA_RSRC(Oh, (uint32_t)Lq * rso);
-      const auto rl = FA_RSRC(Lh, (uint32_t)Lq * 4u);
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const bool in = qrow < Lq;
+    // lane part of the offset in the register; the part fixed at compile
+    // time goes in the instruction's scalar offset (left to itself the
+    // compiler keeps one register per store)
+    const uint32_t oend = (uint32_t)Lq * rso, lend = (uint32_t)Lq * 4u;
+    const uint32_t orow = (in ? (uint32_t)qrow * rso : oend) + (uint32_t)(16 * hh);
+    const uint32_t lrow = in ? (uint32_t)qrow * 4u : lend;
+    const auto ro = FA_RSRC(Oh, oend);
+    const auto rl = FA_RSRC(Lh, lend);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
 #pragma unroll
-      for (int jd = 0; jd < NDB; ++jd)
+    for (int jd = 0; jd < NDB; ++jd)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const f32x16& a = o[jd];
-          const int r0 = 8 * g;
-          const u32x4 w = {Ops<T>::pack2(a[r0 + 0] * inv, a[r0 + 1] * inv),
-                           Ops<T>::pack2(a[r0 + 2] * inv, a[r0 + 3] * inv),
-                           Ops<T>::pack2(a[r0 + 4] * inv, a[r0 + 5] * inv),
-                           Ops<T>::pack2(a[r0 + 6] * inv, a[r0 + 7] * inv)};
-          // accumulator element r0+e of lane (i, hh) is d = 32jd + 16g + 8hh + e
-          __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_frag_off<D>(qrow, jd, g, hh, rso), 0, 0);
-        }
-      if (hh == 0) {
-        const float l2 = ltot > 0.f ? (b + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l2), rl,
-                                              (uint32_t)qrow * 4u, 0, 0);
+      for (int g = 0; g < 2; ++g) {
+        const f32x16& a = o[jd];
+        const int r0 = 8 * g;
+        const u32x4 w = {Ops<T>::pack2(a[r0 + 0] * inv, a[r0 + 1] * inv),
+                         Ops<T>::pack2(a[r0 + 2] * inv, a[r0 + 3] * inv),
+                         Ops<T>::pack2(a[r0 + 4] * inv, a[r0 + 5] * inv),
+                         Ops<T>::pack2(a[r0 + 6] * inv, a[r0 + 7] * inv)};
+        // accumulator element r0+e of lane (i, hh) is d = 32jd + 16g + 8hh + e
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, orow, (int)(o_frag_off<D>(0, jd, g, 0, rso)), 0);
       }
-    }
-    if (DIAG && n_events) atomicAdd(events, (unsigned long long)n_events);
+    const float l2 = ltot > 0.f ? (b + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l2), rl, lrow, 0, 0);
+  }
+  // the rescale events counted so far, added to *events
+  __device__ __forceinline__ void flush_events(unsigned long long* events) const {
+    if (DIAG && n_events && lane == 0) atomicAdd(events, (unsigned long long)n_events);
+  }
+  __device__ __forceinline__ void epilogue(unsigned long long* events) {
+    store_rows();
+    flush_events(events);
   }
 };
 

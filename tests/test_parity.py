@@ -226,14 +226,15 @@ def _diag(qb, kb, vb, dtype, causal, scale, thr, variant=0):
 @pytest.mark.parametrize("name", ["long", "bat"])
 def test_persistent_equals_pingpong_full_size(name):
     """The persistent form runs the ping-pong kernel's per-item code with the
-    work items in another order, so at the full workload sizes its output is the
-    ping-pong kernel's bit for bit."""
+    work items in another order, so at the full workload sizes its output, and
+    its count of rescale events, are the ping-pong kernel's bit for bit."""
     w = W.WORKLOADS[name]
     _banner(f"persistent vs ping-pong, {name}: B={w.B} H={w.H} S={w.S} D={w.D}")
     qb, kb, vb = W.make_inputs(w)
-    o2, l2, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, diag.VARIANT_PING_PONG)
-    o5, l5, _ = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, diag.VARIANT_PERSISTENT)
+    o2, l2, e2 = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, diag.VARIANT_PING_PONG)
+    o5, l5, e5 = _diag(qb, kb, vb, w.dtype, w.causal, w.scale, 8, diag.VARIANT_PERSISTENT)
     assert np.array_equal(o2, o5) and np.array_equal(l2, l5)
+    assert e5 == e2, (e5, e2)
 
 
 @pytest.mark.parametrize("kernel", sorted(VARIANTS))
@@ -263,8 +264,7 @@ def test_lagging_and_eager_rescale_both_match(D, kernel):
     # the float64 model of the algorithm, same KV tile size
     # KV tile of the forced kernel: the eight-wave kernel's from the tile
     # query on a grid large enough for fa_fwd to pick it
-    bn = {"k4": 64, "pp": fa.fa_fwd_tile(D, 1, 256, 1024)[1],
-          "ps": fa.fa_fwd_tile(D, 1, 256, 1024)[1]}[kernel]
+    bn = 64 if kernel == "k4" else fa.fa_fwd_tile(D, 1, 256, 1024)[1]
     model = {8: 0, 0: 0}
     for h in range(w.H):
         q, k, v = (W.decode(x[0, h], dt) for x in (qb, kb, vb))

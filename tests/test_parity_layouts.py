@@ -99,6 +99,34 @@ def test_no_keys_gives_zero_rows():
         assert torch.all(o == 0) and torch.all(torch.isneginf(lse)), causal
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_huge_output_row_stride(causal, D):
+    """One query row and an output row stride of 2^29 elements (2^30 bytes,
+    inside the per-head limit): the kernel's padding rows past the last query
+    row would land at byte offsets that are multiples of 2^30, which wrap to
+    row 0 in 32-bit arithmetic; they must be dropped, so row 0 keeps its own
+    result (O's buffer holds just that row)."""
+    dtype, Sk = W.BF16, 40
+    tag = f"row stride 2^29 causal={causal} D={D}"
+    _banner(tag)
+    qb, kb, vb = _bits((1, 1, 1, D), dtype, 90 + D), _bits((1, 1, Sk, D), dtype, 91 + D), \
+        _bits((1, 1, Sk, D), dtype, 92 + D)
+    q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
+    o = torch.full((D,), 3.0, dtype=torch.bfloat16, device=device())
+    lse = torch.zeros((1,), dtype=torch.float32, device=device())
+    st = [D, D, D, Sk * D, Sk * D, D, Sk * D, Sk * D, D, D, D, 1 << 29, 1, 1]
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    fa.fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      1, 1, 1, Sk, D, causal, scale, torch.cuda.current_stream().cuda_stream,
+                      W.DTYPE_CODE[dtype], st)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_fwd(W.decode(qb, dtype), W.decode(kb, dtype),
+                                        W.decode(vb, dtype), causal, scale)
+    _assert_close(o_to_f64(o.view(1, 1, 1, D)), lse.cpu().numpy().astype(np.float64).reshape(1, 1, 1),
+                  o_ref, l_ref, dtype, tag)
+
+
 # ------------------------------------------------------------ strided layouts
 
 @pytest.mark.parametrize("causal", [False, True])
