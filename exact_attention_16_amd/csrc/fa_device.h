@@ -198,7 +198,8 @@ template <class C, bool CAUSAL, int THR> struct RowState {
   __device__ __forceinline__ bool locate(const Problem& P, int sub, HeadRows* hr, int id) {
     const int tid = threadIdx.x;
     lane = tid & 63;
-    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // (the key-split kernel runs several groups of C::NW waves on the same rows)
+    wave = __builtin_amdgcn_readfirstlane((tid >> 6) % C::NW);
     hh = lane >> 5;
     c = P.c;
     int bh;

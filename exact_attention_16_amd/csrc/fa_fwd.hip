@@ -139,10 +139,11 @@ int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n, int* thr
   const int SS = S < 0 ? 0 : S;
   const bool pp = D == 64 ? fa::use_pingpong<64>(BH, SS, fa::kAuto)
                           : fa::use_pingpong<128>(BH, SS, fa::kAuto);
-  const int bm = pp ? 256 : 128;
+  const bool split = !pp && D == 64 && fa::use_split<64>(BH, SS, fa::kAuto);
+  const int bm = pp ? 256 : (split ? 64 : 128);
   if (block_m) *block_m = bm;
   if (block_n) *block_n = pp ? (D == 64 ? fa::Cfg8<64>::BN : fa::Cfg8<128>::BN) : 64;
-  if (threads) *threads = pp ? 512 : 256;
+  if (threads) *threads = (pp || split) ? 512 : 256;
   if (work_groups) *work_groups = (long long)BH * fa::num_q_tiles(SS, bm);
   return FA_OK;
 }

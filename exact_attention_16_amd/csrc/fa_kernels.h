@@ -21,6 +21,7 @@
 #include "../../include/fa_fwd.h"
 #include "fa_device.h"
 #include "fa_pingpong.h"
+#include "fa_split.h"
 #include "fa_wave.h"
 
 namespace fa {
@@ -181,17 +182,29 @@ fa_fwd_k4(const Problem P) {
 // ------------------------------------------------------------------- host
 
 // Kernel choice: the ping-pong kernel when its 256-row tiles give at least
-// one work-group per compute unit, else the four-wave kernel.
+// one work-group per compute unit; else the four-wave kernel when its
+// 128-row tiles do, or at D = 128, or for sequences under kSplitMinKeys
+// (four KV tiles: there the key-split kernel's merge costs more than the
+// shorter chain saves); else the key-split kernel (64-row tiles, four
+// groups splitting the keys).
 constexpr long long kPingPongMinGroups = 256;
+constexpr long long kFourWaveMinGroups = 256;
+constexpr int kSplitMinKeys = 256;
 
-// Kernel variants (the diagnostic entry point can force one; 3 and 4 are
+// Kernel variants (the diagnostic entry point can force one; 3, 4 and 6 are
 // retired kernel numbers)
-enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kPersistent = 5 };
+enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kPersistent = 5, kSplit = 7 };
 
 template <int D> static inline bool use_pingpong(int BH, int S, int variant) {
-  if (variant == kFourWave) return false;
+  if (variant == kFourWave || variant == kSplit) return false;
   if (variant == kPingPong || variant == kPersistent) return true;
   return (long long)num_q_tiles(S, Cfg8<D>::BM) * BH >= kPingPongMinGroups;
+}
+// (with the ping-pong kernel ruled out)
+template <int D> static inline bool use_split(int BH, int S, int variant) {
+  if (D != 64 || variant == kFourWave) return false;
+  if (variant == kSplit) return true;
+  return S >= kSplitMinKeys && (long long)num_q_tiles(S, Cfg4<D>::BM) * BH < kFourWaveMinGroups;
 }
 
 // Work-groups of the persistent kernel: one per CU of the current device,
@@ -220,6 +233,13 @@ static int launch_one(Problem P, hipStream_t stream, int variant) {
     P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);
     hipLaunchKernelGGL((fa_fwd_pp<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
                        dim3(Cfg8<D>::threads), 0, stream, P);
+  } else if (use_split<D>(BH, P.Sq, variant)) {
+    if constexpr (D == 64) {
+      P.nqt = num_q_tiles(P.Sq, CfgSplit<D>::BM);
+      hipLaunchKernelGGL((fa_fwd_split<T, D, CAUSAL, THR, DIAG>),
+                         dim3((unsigned)P.nqt * (unsigned)BH),
+                         dim3(CfgSplit<D>::threads * kSplitGroups), 0, stream, P);
+    }
   } else {
     P.nqt = num_q_tiles(P.Sq, Cfg4<D>::BM);
     hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),

@@ -169,7 +169,10 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * head dimension D: query rows per work-group, keys per KV tile, threads per
  * work-group, and the number of work-groups launched. fa_fwd runs the
  * eight-wave kernel (256 rows; 96 keys per tile at D=128, 128 at D=64) when
- * B*H*ceil(S/256) >= 256, else the four-wave kernel (128 rows, 64 keys).
+ * B*H*ceil(S/256) >= 256; else the four-wave kernel (128 rows, 64 keys)
+ * when B*H*ceil(S/128) >= 256, D = 128 or S < 256; else (D = 64) the
+ * key-split kernel (64 rows, 64 keys, 512 threads: four groups of two
+ * waves, each taking every fourth KV tile, merged at the end).
  * The same choice, with S the query length, applies to fa_fwd_strided and
  * fa_fwd_varlen.
  * Any output pointer may be NULL. Returns FA_ERR_UNSUPPORTED for D not in

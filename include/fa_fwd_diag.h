@@ -33,17 +33,20 @@ extern "C" {
  *                    work-group), 2 = the eight-wave ping-pong kernel (256
  *                    rows), 5 = the ping-pong kernel in persistent form (one
  *                    work-group per CU of the current device, rounded down to
- *                    a multiple of 8, each running query tiles in turn).
- *                    3 and 4 are retired kernel numbers (FA_ERR_ARG). Every
- *                    variant computes the same result to rounding.
+ *                    a multiple of 8, each running query tiles in turn), 7 =
+ *                    the key-split kernel (D = 64 only: 64 query rows per
+ *                    work-group, four groups of two waves each taking every
+ *                    fourth KV tile, merged at the end). 3, 4 and 6 are
+ *                    retired kernel numbers (FA_ERR_ARG). Every variant
+ *                    computes the same result to rounding.
  *   rescale_events   device pointer to one unsigned 64-bit counter, owned by
  *                    the caller; the kernel atomically adds the number of
  *                    (query row, KV tile) pairs whose running max moved
  *                    after the row's first tile. Not cleared by the library.
  * Errors: those of fa_fwd; threshold_log2 not 0 or 8, or variant not 0, 1,
- * 2 or 5: FA_ERR_ARG; NULL rescale_events: FA_ERR_NULL; rescale_events not
- * 8-byte aligned: FA_ERR_ALIGN; the CU count of the current device not
- * readable (variant 5): FA_ERR_HIP.
+ * 2, 5 or 7, or 7 with D = 128: FA_ERR_ARG; NULL rescale_events:
+ * FA_ERR_NULL; rescale_events not 8-byte aligned: FA_ERR_ALIGN; the CU count
+ * of the current device not readable (variant 5): FA_ERR_HIP.
  */
 int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int S, int D, int causal, float scale,
