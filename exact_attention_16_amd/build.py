@@ -3,11 +3,13 @@
 * exact_attention_16_amd/libfa_fwd.so -- the product library (include/fa_fwd.h);
 * exact_attention_16_amd/libfa_fwd_diag.so -- the diagnostic library the tests
   load beside it (include/fa_fwd_diag.h: the same kernels with a
-  rescale-event counter, both lag thresholds, and a forced kernel choice).
+  rescale-event counter, both lag thresholds, and a forced kernel choice);
+* exact_attention_16_amd/libfa_probe.so -- the issue-rate probes
+  (include/fa_probe.h), run by exact_attention_16_amd.probe.
 
 Usage: python -m exact_attention_16_amd.build [--verbose] [--save-temps DIR]
 
-Compiles both (in parallel) every time it is called. The code objects target
+Compiles all three (in parallel) every time it is called. The code objects target
 gfx950 only.
 Packed fp32 VALU instructions are disabled for the device code
 (-packed-fp32-ops); the host pass warns that it does not know the feature,
@@ -27,6 +29,8 @@ SRCS = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_fwd_fp8.hip")]
 OUT = os.path.join(HERE, "libfa_fwd.so")
 DIAG_SRCS = [os.path.join(HERE, "csrc", "fa_fwd_diag.hip")]
 DIAG_OUT = os.path.join(HERE, "libfa_fwd_diag.so")
+PROBE_SRCS = [os.path.join(HERE, "csrc", "fa_probe.hip")]
+PROBE_OUT = os.path.join(HERE, "libfa_probe.so")
 ARCH = "gfx950"
 
 
@@ -61,9 +65,9 @@ def _command(srcs, out, save_temps):
 def scratch_use(remarks: str) -> list[tuple[str, int]]:
     """Kernels whose resource-usage remarks report scratch memory (register
     spills), with the bytes per lane. No kernel here may spill: besides the
-    cost, the stream form of the ping-pong kernel counts its vector-memory
-    instructions exactly in its waits, and spill loads and stores would make
-    those waits too short."""
+    cost, the ping-pong kernel counts its vector-memory instructions exactly
+    in its waits (a constant count of DMA issues left in flight), and spill
+    loads and stores would make those waits too short."""
     out, name = [], None
     for line in remarks.splitlines():
         if "Function Name:" in line:
@@ -77,9 +81,9 @@ def scratch_use(remarks: str) -> list[tuple[str, int]]:
 
 def build(verbose: bool = False, save_temps: str | None = None, resource_usage: bool = False,
           diag: bool = True) -> str:
-    """Compile the product library (and the diagnostic one unless diag=False);
-    returns the product library's path."""
-    jobs = [(SRCS, OUT)] + ([(DIAG_SRCS, DIAG_OUT)] if diag else [])
+    """Compile the product library (and the diagnostic and probe libraries
+    unless diag=False); returns the product library's path."""
+    jobs = [(SRCS, OUT)] + ([(DIAG_SRCS, DIAG_OUT), (PROBE_SRCS, PROBE_OUT)] if diag else [])
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
     procs = []
@@ -116,7 +120,7 @@ def main(argv=None) -> int:
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true")
     ap.add_argument("--save-temps", default=None)
-    ap.add_argument("--no-diag", action="store_true", help="build the product library only")
+    ap.add_argument("--no-diag", action="store_true", help="build the product library only (no diagnostic or probe library)")
     a = ap.parse_args(argv)
     p = build(a.verbose, a.save_temps, a.resource_usage, diag=not a.no_diag)
     print(p)

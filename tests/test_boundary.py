@@ -9,11 +9,12 @@ import pytest
 
 import diag
 import exact_attention_16_amd as fa
-from exact_attention_16_amd import _lib
+from exact_attention_16_amd import _lib, probe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
 DIAG_HEADER = os.path.join(ROOT, "include", "fa_fwd_diag.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "fa_probe.h")
 
 OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG, LAYOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
@@ -38,6 +39,7 @@ def test_header_declares_the_entry_points():
                            "fa_fwd_varlen", "fa_fwd_kt", "fa_fwd_fp8", "fa_fwd_tile",
                            "fa_strerror", "fa_version"}
     assert _declared(DIAG_HEADER) == {"fa_fwd_diag"}
+    assert _declared(PROBE_HEADER) == {"fa_probe_run"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -53,6 +55,11 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(dlib, name), name
         assert name in diag.SIGNATURES, name
     assert _exported(diag.DIAG_PATH) == _declared(DIAG_HEADER)
+    plib = probe.load_probe()
+    for name in _declared(PROBE_HEADER):
+        assert hasattr(plib, name), name
+        assert name in probe.SIGNATURES, name
+    assert _exported(probe.PROBE_PATH) == _declared(PROBE_HEADER)
 
 
 def _stubs(path):
@@ -171,6 +178,28 @@ def test_diag_validation():
     e = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 0, 64, 0, 0.1, None, 0)
     for variant in (0, 1, 2, 5):
         assert diag.fa_fwd_diag(*e, 8, variant, ev, check=False) == OK
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((probe.NONE, 1, probe.NONE, 1, 1, 0), ARG),      # no stream at all
+    ((6, 1, probe.NONE, 0, 1, 0), ARG),               # unknown stream
+    ((probe.FMA, 1, -1, 1, 1, 0), ARG),
+    ((probe.FMA, 0, probe.NONE, 0, 1, 0), ARG),       # iters out of range
+    ((probe.FMA, (1 << 20) + 1, probe.NONE, 0, 1, 0), ARG),
+    ((probe.FMA, 1, probe.EXP, 0, 2, 0), ARG),
+    ((probe.FMA, 1, probe.NONE, 0, 0, 0), ARG),       # waves per SIMD out of range
+    ((probe.FMA, 1, probe.NONE, 0, 5, 0), ARG),
+    ((probe.MIX, 1, probe.NONE, 0, 1, 9), ARG),       # mix out of range
+    ((probe.MIX, 1, probe.NONE, 0, 1, -1), ARG),
+])
+def test_probe_validation(args, expect):
+    assert probe.fa_probe_run(*args, 0x20000000000, None, check=False) == expect
+
+
+def test_probe_null_and_alignment():
+    assert probe.fa_probe_run(probe.FMA, 1, probe.NONE, 0, 1, 0, 0, None, check=False) == NULL
+    assert probe.fa_probe_run(probe.FMA, 1, probe.NONE, 0, 1, 0, 0x20000000004, None,
+                              check=False) == ALIGN
 
 
 def test_error_raises_with_name():
