@@ -202,8 +202,10 @@ def clock_fields(tflops: float, peak: float, clk: dict) -> dict:
 def kernel_name(w) -> str:
     """The kernel fa_fwd launches for this workload (from the tile query)."""
     import exact_attention_16_amd as fa
-    bm, bn, threads, groups = fa.fa_fwd_tile(w.D, w.B, w.H, w.S)
+    bm, bn, threads, groups = fa.fa_fwd_tile(w.D, w.B, w.H, w.S, w.causal)
     kind = {256: "fa_fwd_pp", 128: "fa_fwd_k4", 64: "fa_fwd_split"}[bm]
+    if bm == 256 and bn == 64:
+        kind = "fa_fwd_occ4"
     return (f"{kind}<{w.dtype},D={w.D},causal={int(w.causal)}> "
             f"({groups} work-groups x {threads} threads, {bm} query rows, {bn}-key tiles)")
 

@@ -39,7 +39,7 @@ SIGNATURES = {
     "fa_fwd_varlen": (_I, [_P] * 7 + [_I] * 8 + [_F, _P, _I, _P]),
     "fa_fwd_kt": (_I, _FWD_ARGS + [_I]),
     "fa_fwd_fp8": (_I, [_P] * 5 + [_I] * 5 + [_F] * 4 + [_P]),
-    "fa_fwd_tile": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
+    "fa_fwd_tile": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
                          ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_longlong)]),
     "fa_strerror": (ctypes.c_char_p, [_I]),
     "fa_version": (_I, []),
@@ -129,11 +129,11 @@ def fa_fwd_fp8(q, k, v, o, lse, B, H, S, D, causal, scale, descale_q, descale_k,
     return _check(st, "fa_fwd_fp8") if check else st
 
 
-def fa_fwd_tile(D, B=0, H=0, S=0):
+def fa_fwd_tile(D, B=0, H=0, S=0, causal=False):
     """(block_m, block_n, threads, work_groups) for head dim D."""
     bm, bn, th = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     wg = ctypes.c_longlong()
-    _check(load().fa_fwd_tile(D, B, H, S, ctypes.byref(bm), ctypes.byref(bn),
+    _check(load().fa_fwd_tile(D, B, H, S, int(causal), ctypes.byref(bm), ctypes.byref(bn),
                               ctypes.byref(th), ctypes.byref(wg)), "fa_fwd_tile")
     return bm.value, bn.value, th.value, wg.value
 

@@ -132,18 +132,21 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   return fa::launch_dtype(P, D, causal, dtype, stream);
 }
 
-int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n, int* threads,
+int fa_fwd_tile(int D, int B, int H, int S, int causal, int* block_m, int* block_n, int* threads,
                 long long* work_groups) {
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
   const int BH = (B < 0 || H < 0) ? 0 : B * H;
   const int SS = S < 0 ? 0 : S;
-  const bool pp = D == 64 ? fa::use_pingpong<64>(BH, SS, fa::kAuto)
-                          : fa::use_pingpong<128>(BH, SS, fa::kAuto);
-  const bool split = !pp && D == 64 && fa::use_split<64>(BH, SS, fa::kAuto);
-  const int bm = pp ? 256 : (split ? 64 : 128);
+  const bool occ = D == 64 && (causal ? fa::use_occ4<64, true>(BH, SS, fa::kAuto)
+                                      : fa::use_occ4<64, false>(BH, SS, fa::kAuto));
+  const bool pp = !occ && (D == 64 ? fa::use_pingpong<64>(BH, SS, fa::kAuto)
+                                   : fa::use_pingpong<128>(BH, SS, fa::kAuto));
+  const bool split = !occ && !pp && D == 64 && fa::use_split<64>(BH, SS, fa::kAuto);
+  const int bm = (occ || pp) ? 256 : (split ? 64 : 128);
   if (block_m) *block_m = bm;
   if (block_n) *block_n = pp ? (D == 64 ? fa::Cfg8<64>::BN : fa::Cfg8<128>::BN) : 64;
-  if (threads) *threads = (pp || split) ? 512 : 256;
+  if (threads) *threads = (occ || pp || split) ? 512 : 256;
   if (work_groups) *work_groups = (long long)BH * fa::num_q_tiles(SS, bm);
   return FA_OK;
 }
@@ -185,6 +188,6 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   return fa::launch_fp8(P, D, causal, stream);
 }
 
-int fa_version(void) { return 400; }
+int fa_version(void) { return 500; }
 
 }  // extern "C"

@@ -26,7 +26,7 @@ int fa_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse
   if (r != FA_OK) return r;
   if (threshold_log2 != 0 && threshold_log2 != 8) return FA_ERR_ARG;
   if (variant != fa::kAuto && variant != fa::kFourWave && variant != fa::kPingPong &&
-      variant != fa::kPersistent && !(variant == fa::kSplit && D == 64))
+      variant != fa::kPersistent && !((variant == fa::kSplit || variant == fa::kOcc4) && D == 64))
     return FA_ERR_ARG;
   if (!rescale_events) return FA_ERR_NULL;
   if (((uintptr_t)rescale_events & 7) != 0) return FA_ERR_ALIGN;

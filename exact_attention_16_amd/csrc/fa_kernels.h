@@ -11,6 +11,10 @@
 //  * fa_fwd_k4 (four waves, 128 query rows), for grids too small to fill the
 //    chip with 256-row tiles: each wave overlaps the next tile's K.Q^T (and,
 //    at D=64, the previous tile's P.V) with its own current softmax.
+//  * fa_fwd_split (fa_split.h), for small grids at D = 64: four groups of
+//    two waves split each query tile's KV tiles, merged in LDS.
+//  * fa_fwd_occ4 (fa_occ4.h), D = 64 without the causal mask on grids that
+//    fill the chip: eight waves, 64-key tiles, four waves per SIMD.
 //  * fa_fwd_pp_kt: the ping-pong body on a K given transposed ([D, S]).
 //  * fa_fwd_pp_persist: the ping-pong body in persistent form.
 #pragma once
@@ -21,6 +25,7 @@
 #include "../../include/fa_fwd.h"
 #include "fa_device.h"
 #include "fa_pingpong.h"
+#include "fa_occ4.h"
 #include "fa_split.h"
 #include "fa_wave.h"
 
@@ -181,8 +186,10 @@ fa_fwd_k4(const Problem P) {
 
 // ------------------------------------------------------------------- host
 
-// Kernel choice: the ping-pong kernel when its 256-row tiles give at least
-// one work-group per compute unit; else the four-wave kernel when its
+// Kernel choice: at D = 64 without the causal mask, the four-waves-per-SIMD
+// kernel where the ping-pong kernel would run; else the ping-pong kernel
+// when its 256-row tiles give at least one work-group per compute unit;
+// else the four-wave kernel when its
 // 128-row tiles do, or at D = 128, or for sequences under kSplitMinKeys
 // (four KV tiles: there the key-split kernel's merge costs more than the
 // shorter chain saves); else the key-split kernel (64-row tiles, four
@@ -193,12 +200,18 @@ constexpr int kSplitMinKeys = 256;
 
 // Kernel variants (the diagnostic entry point can force one; 3, 4 and 6 are
 // retired kernel numbers)
-enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kPersistent = 5, kSplit = 7 };
+enum Variant { kAuto = 0, kFourWave = 1, kPingPong = 2, kPersistent = 5, kSplit = 7, kOcc4 = 8 };
 
 template <int D> static inline bool use_pingpong(int BH, int S, int variant) {
-  if (variant == kFourWave || variant == kSplit) return false;
+  if (variant == kFourWave || variant == kSplit || variant == kOcc4) return false;
   if (variant == kPingPong || variant == kPersistent) return true;
   return (long long)num_q_tiles(S, Cfg8<D>::BM) * BH >= kPingPongMinGroups;
+}
+// (checked first)
+template <int D, bool CAUSAL> static inline bool use_occ4(int BH, int S, int variant) {
+  if (D != 64) return false;
+  if (variant == kOcc4) return true;
+  return variant == kAuto && !CAUSAL && use_pingpong<D>(BH, S, kAuto);
 }
 // (with the ping-pong kernel ruled out)
 template <int D> static inline bool use_split(int BH, int S, int variant) {
@@ -228,6 +241,14 @@ static int launch_one(Problem P, hipStream_t stream, int variant) {
       if (g <= 0) return FA_ERR_HIP;
       hipLaunchKernelGGL((fa_fwd_pp_persist<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)g),
                          dim3(Cfg8<D>::threads), 0, stream, P);
+    }
+  } else if (use_occ4<D, CAUSAL>(BH, P.Sq, variant)) {
+    // the product library runs it without the causal mask only
+    if constexpr (D == 64 && (!CAUSAL || DIAG)) {
+      P.nqt = num_q_tiles(P.Sq, CfgOcc4<D>::BM);
+      hipLaunchKernelGGL((fa_fwd_occ4<T, D, CAUSAL, THR, DIAG>),
+                         dim3((unsigned)P.nqt * (unsigned)BH), dim3(CfgOcc4<D>::threads), 0,
+                         stream, P);
     }
   } else if (use_pingpong<D>(BH, P.Sq, variant)) {
     P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);

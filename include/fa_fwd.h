@@ -165,20 +165,22 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   const long long* strides);
 
 /*
- * fa_fwd_tile -- the tile shape fa_fwd uses for a call with (B, H, S) at
- * head dimension D: query rows per work-group, keys per KV tile, threads per
- * work-group, and the number of work-groups launched. fa_fwd runs the
- * eight-wave kernel (256 rows; 96 keys per tile at D=128, 128 at D=64) when
- * B*H*ceil(S/256) >= 256; else the four-wave kernel (128 rows, 64 keys)
- * when B*H*ceil(S/128) >= 256, D = 128 or S < 256; else (D = 64) the
- * key-split kernel (64 rows, 64 keys, 512 threads: four groups of two
- * waves, each taking every fourth KV tile, merged at the end).
- * The same choice, with S the query length, applies to fa_fwd_strided and
- * fa_fwd_varlen.
+ * fa_fwd_tile -- the tile shape fa_fwd uses for a call with (B, H, S,
+ * causal) at head dimension D: query rows per work-group, keys per KV tile,
+ * threads per work-group, and the number of work-groups launched. fa_fwd
+ * runs, at D = 64 without the causal mask, the four-waves-per-SIMD kernel
+ * (256 rows, 64 keys, 512 threads, two work-groups per CU) when
+ * B*H*ceil(S/256) >= 256; else the eight-wave ping-pong kernel (256 rows; 96
+ * keys per tile at D=128, 128 at D=64) when B*H*ceil(S/256) >= 256; else the
+ * four-wave kernel (128 rows, 64 keys) when B*H*ceil(S/128) >= 256, D = 128
+ * or S < 256; else (D = 64) the key-split kernel (64 rows, 64 keys, 512
+ * threads: four groups of two waves, each taking every fourth KV tile,
+ * merged at the end). The same choice, with S the query length, applies to
+ * fa_fwd_strided and fa_fwd_varlen.
  * Any output pointer may be NULL. Returns FA_ERR_UNSUPPORTED for D not in
- * {64, 128}.
+ * {64, 128}, FA_ERR_ARG for causal not 0 or 1.
  */
-int fa_fwd_tile(int D, int B, int H, int S, int* block_m, int* block_n,
+int fa_fwd_tile(int D, int B, int H, int S, int causal, int* block_m, int* block_n,
                 int* threads, long long* work_groups);
 
 /*

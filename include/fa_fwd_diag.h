@@ -36,15 +36,19 @@ extern "C" {
  *                    a multiple of 8, each running query tiles in turn), 7 =
  *                    the key-split kernel (D = 64 only: 64 query rows per
  *                    work-group, four groups of two waves each taking every
- *                    fourth KV tile, merged at the end). 3, 4 and 6 are
- *                    retired kernel numbers (FA_ERR_ARG). Every variant
- *                    computes the same result to rounding.
+ *                    fourth KV tile, merged at the end), 8 = the
+ *                    four-waves-per-SIMD kernel (D = 64 only: 256 query
+ *                    rows, 64-key tiles, two work-groups per CU; fa_fwd
+ *                    runs it without the causal mask, the test hook with
+ *                    either). 3, 4 and 6 are retired kernel numbers
+ *                    (FA_ERR_ARG). Every variant computes the same result to
+ *                    rounding.
  *   rescale_events   device pointer to one unsigned 64-bit counter, owned by
  *                    the caller; the kernel atomically adds the number of
  *                    (query row, KV tile) pairs whose running max moved
  *                    after the row's first tile. Not cleared by the library.
  * Errors: those of fa_fwd; threshold_log2 not 0 or 8, or variant not 0, 1,
- * 2, 5 or 7, or 7 with D = 128: FA_ERR_ARG; NULL rescale_events:
+ * 2, 5, 7 or 8, or 7 or 8 with D = 128: FA_ERR_ARG; NULL rescale_events:
  * FA_ERR_NULL; rescale_events not 8-byte aligned: FA_ERR_ALIGN; the CU count
  * of the current device not readable (variant 5): FA_ERR_HIP.
  */

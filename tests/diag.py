@@ -18,6 +18,7 @@ VARIANT_FOUR_WAVE = 1
 VARIANT_PING_PONG = 2
 VARIANT_PERSISTENT = 5
 VARIANT_SPLIT = 7
+VARIANT_OCC4 = 8
 
 SIGNATURES = {"fa_fwd_diag": (ctypes.c_int, _lib._FWD_ARGS + [ctypes.c_int] * 3 + [ctypes.c_void_p])}
 

@@ -710,11 +710,42 @@ static void check_il_schedule(int ntiles) {
   }
 }
 
+// The two-stage schedule of the four-waves-per-SIMD kernel (and of each
+// group of the key-split kernel, over its own tiles): step j reads K(j) and
+// V(j) from stage j % 2; at its top it issues the DMA of tile j+1 into the
+// other stage, whose last reader was step j-1 (every wave has passed the
+// barrier that ends step j-1); the wait before the barrier that ends step j
+// lands that DMA.
+static void check_two_stage(int ntiles) {
+  int tile[2] = {0, -2};       // tile held by the stage (the prologue loads tile 0)
+  int landed[2] = {1, 1};      // whether its DMA has landed
+  int last_read[2] = {-1, -2}; // step that last read the stage
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j % 2, oth = 1 - cur;
+    if (j + 1 < ntiles) {
+      CHECK(last_read[oth] <= j - 1, "two-stage: stage %d overwritten while read at %d", oth, j);
+      tile[oth] = j + 1;
+      landed[oth] = 0;
+    }
+    CHECK(tile[cur] == j && landed[cur], "two-stage: tile %d not resident at step %d", j, j);
+    last_read[cur] = j;
+    landed[oth] = 1;  // the wait before the barrier ending step j
+  }
+}
+
+// the key-split kernel's per-group configuration (two waves, 64 rows,
+// 64-key tiles) and the four-waves-per-SIMD kernel's (eight waves, 256 rows,
+// 64-key tiles)
+using CfgSplitG = Cfg<64, 2, 64>;
+using CfgOcc = Cfg<64, 8, 64>;
+
 int main() {
   check_lds<Cfg4<64>>();
   check_lds<Cfg4<128>>();
   check_lds<Cfg8<64>>();
   check_lds<Cfg8<128>>();
+  check_lds<CfgSplitG>();
+  check_lds<CfgOcc>();
   check_tile_map();
   std::printf("work-group map: every head-group size: checked\n");
   // persistent work-groups: every item exactly once, ids rising per group
@@ -757,15 +788,21 @@ int main() {
       check_global<Cfg4<128>>(s[0], s[1], s[2], causal);
       check_global<Cfg8<64>>(s[0], s[1], s[2], causal);
       check_global<Cfg8<128>>(s[0], s[1], s[2], causal);
+      check_global<CfgSplitG>(s[0], s[1], s[2], causal);
+      check_global<CfgOcc>(s[0], s[1], s[2], causal);
     }
   check_lengths<Cfg4<64>>();
   check_lengths<Cfg4<128>>();
   check_lengths<Cfg8<64>>();
   check_lengths<Cfg8<128>>();
+  check_lengths<CfgSplitG>();
+  check_lengths<CfgOcc>();
   std::printf("query/key length pairs (bottom-right causal), padded rows: checked\n");
   // full-size shapes (O coverage tracked up to 64M elements)
   check_global<Cfg4<64>>(1, 16, 1024, true);
   check_global<Cfg8<64>>(10, 64, 1024, false);
+  check_global<CfgOcc>(10, 64, 1024, false);
+  check_global<CfgSplitG>(1, 16, 1024, true);
   check_global<Cfg8<128>>(2, 16, 8192, true);
   check_global<Cfg8<128>>(1, 8, 16384, true);
   check_global<Cfg4<128>>(1, 1, 65536, true);
@@ -773,6 +810,8 @@ int main() {
   // interleaved eight-wave work-group (the 8-bit kernel's body)
   for (int ntiles = 1; ntiles <= 40; ++ntiles) check_il_schedule(ntiles);
   std::printf("interleaved schedule: ntiles 1..40: checked\n");
+  for (int ntiles = 1; ntiles <= 40; ++ntiles) check_two_stage(ntiles);
+  std::printf("two-stage schedule: ntiles 1..40: checked\n");
   // 8-bit kernels (ping-pong with 128-key tiles, interleaved with 64-key tiles)
   check_lds8<CfgF8>();
   check_lds8<CfgF8i>();

@@ -75,32 +75,39 @@ def test_kernel_launch_stubs_are_defined():
     stubs = _stubs(fa.LIB_PATH)
     # product: 2 kernels (ping-pong, four-wave) x 2 dtypes x 2 head dims x 2
     # masks, the key-split kernel x 2 dtypes x 2 masks (D = 64), the
+    # four-waves-per-SIMD kernel x 2 dtypes (D = 64, no mask), the
     # transposed-K kernel x 2 x 2 x 2, the 8-bit kernel x 2 x 2
-    assert len(stubs) == 32
+    assert len(stubs) == 34
     assert not [l for l in stubs if l.split()[-2] == "U"], "undefined kernel stubs"
     assert not [l for l in stubs if "ELb1EEEv" in l and "fa_fwd_pp_kt" not in l
                 and "fa_fwd_il8" not in l], "instrumented kernels in the product library"
     dstubs = _stubs(diag.DIAG_PATH)
     # diagnostic: 3 kernels (four-wave, ping-pong, persistent) x 2 dtypes x 2
-    # head dims x 2 masks x 2 lag thresholds, the key-split kernel x 2 dtypes
-    # x 2 masks x 2 thresholds (D = 64)
-    assert len(dstubs) == 56
+    # head dims x 2 masks x 2 lag thresholds, the key-split and the
+    # four-waves-per-SIMD kernels x 2 dtypes x 2 masks x 2 thresholds (D = 64)
+    assert len(dstubs) == 64
     assert not [l for l in dstubs if l.split()[-2] == "U"], "undefined kernel stubs"
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 400
+    assert fa.fa_version() == 500
     for st in (OK, NULL, DIM, UNSUP, ALIGN, SCALE, ALIAS, HIP, ARG, LAYOUT):
         assert fa.fa_strerror(st) and fa.fa_strerror(st) != "unknown status"
     assert fa.fa_strerror(12345) == "unknown status"
 
 
 def test_tile_query():
-    # eight-wave kernel once B*H*ceil(S/256) >= 256 work-groups; else the
-    # four-wave kernel once B*H*ceil(S/128) >= 256, at D = 128 or for S < 256;
-    # else the key-split kernel (64 rows, four groups of two waves)
-    assert fa.fa_fwd_tile(128, 2, 16, 8192) == (256, 96, 512, 2 * 16 * 32)
-    assert fa.fa_fwd_tile(64, 10, 64, 1024) == (256, 128, 512, 640 * 4)
+    # at D = 64 without the causal mask the four-waves-per-SIMD kernel (256
+    # rows, 64-key tiles) where the eight-wave kernel would run; eight-wave
+    # kernel once B*H*ceil(S/256) >= 256 work-groups; else the four-wave
+    # kernel once B*H*ceil(S/128) >= 256, at D = 128 or for S < 256; else the
+    # key-split kernel (64 rows, four groups of two waves)
+    assert fa.fa_fwd_tile(128, 2, 16, 8192, True) == (256, 96, 512, 2 * 16 * 32)
+    assert fa.fa_fwd_tile(128, 2, 16, 8192, False) == (256, 96, 512, 2 * 16 * 32)
+    assert fa.fa_fwd_tile(64, 10, 64, 1024) == (256, 64, 512, 640 * 4)
+    assert fa.fa_fwd_tile(64, 10, 64, 1024, True) == (256, 128, 512, 640 * 4)
+    assert fa.fa_fwd_tile(64, 1, 64, 1024, False) == (256, 64, 512, 256)
+    assert fa.fa_fwd_tile(64, 1, 63, 1024, False) == (128, 64, 256, 63 * 8)
     assert fa.fa_fwd_tile(64, 1, 16, 1024) == (64, 64, 512, 16 * 16)
     assert fa.fa_fwd_tile(64, 1, 32, 1024) == (128, 64, 256, 32 * 8)
     assert fa.fa_fwd_tile(128, 1, 64, 1024) == (256, 96, 512, 256)
@@ -110,6 +117,8 @@ def test_tile_query():
     assert fa.fa_fwd_tile(64, 1, 1, 256) == (64, 64, 512, 4)
     with pytest.raises(fa.FaError):
         fa.fa_fwd_tile(96)
+    with pytest.raises(fa.FaError, match="FA_ERR_ARG"):
+        fa.fa_fwd_tile(64, 1, 1, 64, 2)
 
 
 # fake, 16-byte aligned, non-overlapping device addresses: validation never
@@ -170,6 +179,9 @@ def test_diag_validation():
     # the key-split kernel exists at D = 64 only
     args128 = (a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 1, 4, 128, 0, 0.1, None, 0)
     assert diag.fa_fwd_diag(*args128, 8, diag.VARIANT_SPLIT, ev, check=False) == ARG
+    assert diag.fa_fwd_diag(*args128, 8, diag.VARIANT_OCC4, ev, check=False) == ARG
+    for bad in (6, 9):
+        assert diag.fa_fwd_diag(*args, 8, bad, ev, check=False) == ARG
     assert diag.fa_fwd_diag(*args, 8, 0, 0, check=False) == NULL
     assert diag.fa_fwd_diag(*args, 0, 2, ev + 4, check=False) == ALIGN
     # the product checks run first

@@ -25,19 +25,28 @@ def _banner(msg):
 
 
 VARIANTS = {"k4": diag.VARIANT_FOUR_WAVE, "pp": diag.VARIANT_PING_PONG,
-            "ps": diag.VARIANT_PERSISTENT, "sp": diag.VARIANT_SPLIT}
+            "ps": diag.VARIANT_PERSISTENT, "sp": diag.VARIANT_SPLIT, "o4": diag.VARIANT_OCC4}
+# kernels that exist at D = 64 only
+D64_ONLY = ("sp", "o4")
+
+
+def _exists(kernel, D):
+    return D == 64 or kernel not in D64_ONLY
 
 
 def _skip_absent(kernel, D):
-    """The key-split kernel exists at D = 64 only."""
-    if kernel == "sp" and D != 64:
-        pytest.skip("the key-split kernel runs at D = 64 only")
+    """The key-split and four-waves-per-SIMD kernels exist at D = 64 only."""
+    if not _exists(kernel, D):
+        pytest.skip(f"kernel {kernel} runs at D = 64 only")
 
 
-def _auto_kernel(D, B, H, S):
+def _auto_kernel(D, B, H, S, causal):
     """The kernel fa_fwd picks for this shape, by its query rows per
-    work-group."""
-    return {256: "pp", 128: "k4", 64: "sp"}[fa.fa_fwd_tile(D, B, H, S)[0]]
+    work-group and keys per tile."""
+    bm, bn = fa.fa_fwd_tile(D, B, H, S, causal)[:2]
+    if bm == 256 and bn == 64:
+        return "o4"
+    return {256: "pp", 128: "k4", 64: "sp"}[bm]
 
 
 def _check_full(qb, kb, vb, dtype, causal, scale, tag, variant=None):
@@ -108,7 +117,7 @@ def test_kernels_agree(D):
     S, dt = 777, W.F16
     qb, kb, vb = (W.random_bits((2, 2, S, D), dt, 3000 + D + i) for i in range(3))
     res = [_check_full(qb, kb, vb, dt, True, D ** -0.5, f"agree D={D} {k}", VARIANTS[k])
-           for k in sorted(VARIANTS) if not (k == "sp" and D != 64)]
+           for k in sorted(VARIANTS) if _exists(k, D)]
     for other in res[1:]:
         assert np.abs(res[0][0] - other[0]).max() <= O_TOL[dt]
         assert np.abs(res[0][1] - other[1]).max() <= LSE_TOL
@@ -286,14 +295,14 @@ def test_lagging_and_eager_rescale_both_match(D, kernel):
     # the production instantiation of the same kernel gives the same bits
     # (same arithmetic, counter aside)
     o, lse = run(qb, kb, vb, dt, True, w.scale, variant=None)
-    if kernel == _auto_kernel(D, w.B, w.H, w.S):
+    if kernel == _auto_kernel(D, w.B, w.H, w.S, True):
         np.testing.assert_array_equal(o_to_f64(o), res[8][0])
     if kernel == "sp":
         return
     # the float64 model of the algorithm, same KV tile size
     # KV tile of the forced kernel: the eight-wave kernel's from the tile
     # query on a grid large enough for fa_fwd to pick it
-    bn = 64 if kernel == "k4" else fa.fa_fwd_tile(D, 1, 256, 1024)[1]
+    bn = 64 if kernel in ("k4", "o4") else fa.fa_fwd_tile(D, 1, 256, 1024, True)[1]
     model = {8: 0, 0: 0}
     for h in range(w.H):
         q, k, v = (W.decode(x[0, h], dt) for x in (qb, kb, vb))
@@ -318,7 +327,7 @@ def test_ramp_workload_fires_the_lagging_rescale(h):
     qb, kb, vb = W.make_inputs(w)
     q1, k1, v1 = (np.ascontiguousarray(x[:, h:h + 1]) for x in (qb, kb, vb))
     og, lg, ev = _diag(q1, k1, v1, w.dtype, True, w.scale, 8, diag.VARIANT_PING_PONG)
-    bn = fa.fa_fwd_tile(w.D, 1, 256, 1024)[1]  # the ping-pong kernel's KV tile
+    bn = fa.fa_fwd_tile(w.D, 1, 256, 1024, True)[1]  # the ping-pong kernel's KV tile
     q, k, v = (W.decode(x[0, h], w.dtype) for x in (qb, kb, vb))
     model = oracle.online_softmax_attention(q, k, v, True, float(np.float32(w.scale)),
                                             block_n=bn, threshold_log2=8)
