@@ -144,6 +144,8 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 struct HeadRows {
   int Lq, Lk;
   long long q0, k0, v0, o0, l0;
+  int cut_q;   // variable lengths: query rows past the stated maximum
+  bool cut_k;  // variable lengths: more keys than the stated maximum
 };
 // The offsets are read through the constant address space: they do not
 // change during a launch, so the reads are scalar loads of wave-uniform
@@ -160,6 +162,8 @@ __device__ __forceinline__ HeadRows head_rows(const Problem& P, int bb, int h) {
     const int sk = clampi(ck[bb], 0, P.totk), ek = clampi(ck[bb + 1], sk, P.totk);
     r.Lq = min(eq - sq, P.Sq);
     r.Lk = min(ek - sk, P.Sk);
+    r.cut_q = (eq - sq) - r.Lq;
+    r.cut_k = ek - sk > P.Sk;
     r.q0 = sq * P.qs + h * P.qh;
     r.k0 = sk * P.ks + h * P.kh;
     r.v0 = sk * P.vs + h * P.vh;
@@ -168,6 +172,8 @@ __device__ __forceinline__ HeadRows head_rows(const Problem& P, int bb, int h) {
   } else {
     r.Lq = P.Sq;
     r.Lk = P.Sk;
+    r.cut_q = 0;
+    r.cut_k = false;
     r.q0 = bb * P.qb + h * P.qh;
     r.k0 = bb * P.kb + h * P.kh;
     r.v0 = bb * P.vb + h * P.vh;
@@ -217,12 +223,40 @@ template <class C, bool CAUSAL, int THR> struct RowState {
     *hr = head_rows(P, bb, h);
     Lq = hr->Lq;
     Lk = hr->Lk;
+    if (hr->cut_q > 0 || hr->cut_k) {  // rare: a sequence longer than the maxima
+      flag_cut_rows(P, *hr);
+      return false;
+    }
     if (qt * C::BM >= Lq) return false;
     off = Lk - Lq;
     q0w = qt * C::BM + wave * C::RPW + sub * kRowsPerWave;
     qrow = q0w + (lane & 31);
     return true;
   }
+  // Variable lengths, a sequence longer than the stated maxima: its rows past
+  // the maximum query length lie in no work-group's tile, with more keys than
+  // the maximum key length its rows would see only a prefix of them, and
+  // either way the causal alignment (j <= i + Lk - Lq) would use cut
+  // lengths. Such a sequence is not computed: all its rows get NaN in O
+  // (16-bit all-ones: a NaN in fp16 and bf16) and in lse, so the violated
+  // bound shows. Each work-group of the sequence marks its own tile's rows;
+  // the one with the last query tile also marks the rows past the maximum.
+  // Every thread of the work-group takes a share (thread index and block
+  // size).
+  __device__ void flag_cut_rows(const Problem& P, const HeadRows& hr) const {
+    auto mark = [&](int a, int b) {
+      if (b <= a) return;
+      unsigned short* const o = (unsigned short*)P.o + hr.o0;
+      const long long n = (long long)(b - a) * C::D;
+      for (long long i = threadIdx.x; i < n; i += blockDim.x)
+        o[(long long)(a + (int)(i / C::D)) * P.os + (int)(i % C::D)] = 0xFFFFu;
+      for (int r = a + (int)threadIdx.x; r < b; r += (int)blockDim.x)
+        P.lse[hr.l0 + r] = __builtin_nanf("");
+    };
+    mark(qt * C::BM, min(hr.Lq, (qt + 1) * C::BM));
+    if (qt == P.nqt - 1) mark(hr.Lq, hr.Lq + hr.cut_q);
+  }
+
   __device__ __forceinline__ void reset_softmax() {
     b = -INFINITY;
     lsum = 0.f;

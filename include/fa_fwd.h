@@ -144,7 +144,9 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
  *            cu_seqlens_q[b+1]-1 and key tokens cu_seqlens_k[b] ..
  *            cu_seqlens_k[b+1]-1. Read by the kernel; owned by the caller.
  *   max_seqlen_q, max_seqlen_k   upper bounds of the lengths (they size the
- *            grid; a longer sequence is cut to them).
+ *            grid). A sequence longer than max_seqlen_q, or with more keys
+ *            than max_seqlen_k, is not computed: all its rows get NaN in o
+ *            and lse (the other sequences are unaffected).
  *   total_q, total_k   token rows q/o/lse and k/v hold; the kernel clamps
  *            every offset to them, so a bad offset array cannot address
  *            memory outside the tensors.

@@ -243,6 +243,40 @@ def test_varlen_eight_wave_kernel(causal):
         _assert_close(og[qs, h], lg[h, qs], o_ref, l_ref, dtype, f"{tag} b={b} h={h}")
 
 
+@pytest.mark.parametrize("H", [2, 96])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_sequences_past_the_maxima_are_marked(causal, D, H):
+    """A sequence longer than max_seqlen_q, or with more keys than
+    max_seqlen_k, is not computed: all its rows get NaN in O and lse; every
+    other sequence is exact. (H = 2 runs the small-grid kernels, H = 96 the
+    256-row ones.)"""
+    dtype = W.BF16
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    # (query lengths, key lengths, max_q, max_k, sequences past a maximum)
+    cases = [([40, 300, 60], [40, 100, 60], 256, 100, [1]),        # queries past max_q
+             ([40, 90, 60], [40, 90, 200], 128, 128, [2]),         # keys past max_k
+             ([300, 50, 260], [30, 300, 260], 256, 256, [0, 1, 2])]  # both, every sequence
+    for n, (lq, lk, max_q, max_k, cut) in enumerate(cases):
+        _banner(f"varlen past the maxima causal={causal} D={D} H={H} case {n}")
+        cq, ck, qb, kb, vb = _varlen_inputs(lq, lk, H, D, dtype, 150 + 10 * n + D + H)
+        cu_q = torch.from_numpy(cq).to(device())
+        cu_k = torch.from_numpy(ck).to(device())
+        o, lse = fa.attention_varlen(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype),
+                                     cu_q, cu_k, max_q, max_k, causal)
+        torch.cuda.synchronize()
+        og, lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+        bad = np.zeros(int(cq[-1]), dtype=bool)
+        for b in cut:
+            bad[cq[b]:cq[b + 1]] = True
+        assert np.all(np.isnan(og[bad])) and np.all(np.isnan(lg[:, bad])), "cut rows not marked"
+        if (~bad).any():
+            o_ref, l_ref = oracle.attention_varlen(W.decode(qb, dtype), W.decode(kb, dtype),
+                                                   W.decode(vb, dtype), cq, ck, causal, scale)
+            _assert_close(og[~bad], lg[:, ~bad], o_ref[~bad], l_ref[:, ~bad], dtype,
+                          f"varlen rows within the maxima, case {n}")
+
+
 def test_varlen_offsets_past_the_tensors_are_clamped():
     """The last sequence's end offset lies past total_q / total_k: the kernel
     clamps it to the tensors (the sequence ends at the last token row) and
