@@ -263,8 +263,17 @@ static int launch_one(Problem P, hipStream_t stream, int variant) {
     }
   } else {
     P.nqt = num_q_tiles(P.Sq, Cfg4<D>::BM);
+    // At D = 128 the kernel's 64 KiB of LDS let two work-groups share a CU.
+    // Run that way, the work-group whose LDS allocation starts above 64 KiB
+    // (the second on the CU) returned wrong rows in some runs (a few rows of
+    // one wave, several work-groups per launch; never a work-group at LDS
+    // base 0, and never when the two work-groups read the same head). 17 KiB
+    // of unused dynamic LDS keep one work-group per CU (81 KiB > 160 / 2);
+    // the cost on the shapes this kernel serves is 0-2% (7% where the grid
+    // then takes two rounds).
+    const unsigned lds_pad = D == 128 ? 17u * 1024u : 0u;
     hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
-                       dim3(Cfg4<D>::threads), 0, stream, P);
+                       dim3(Cfg4<D>::threads), lds_pad, stream, P);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -110,6 +110,25 @@ def test_many_tiles_all_rows(causal, D, kernel):
                 f"many tiles S={S} D={D} causal={causal} kernel={kernel}", VARIANTS[kernel])
 
 
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_four_wave_d128_many_work_groups_all_rows(dtype):
+    """B=1 H=63 S=1024 D=128 causal: 504 four-wave work-groups, more than one
+    per CU if two could share one. Run two to a CU, the second work-group on a
+    CU returned wrong rows in some launches (a few rows per launch); the
+    launch keeps one per CU. All rows of every head, three launches."""
+    B, H, S, D = 1, 63, 1024, 128
+    assert _auto_kernel(D, B, H, S, True) == "k4"
+    qb, kb, vb = (W.random_bits((B, H, S, D), dtype, 7100 + i) for i in range(3))
+    first = None
+    for rep in range(3):
+        og, lg = _check_full(qb, kb, vb, dtype, True, D ** -0.5,
+                             f"four-wave D=128 H=63 {dtype} launch {rep}")
+        if first is None:
+            first = (og, lg)
+        else:
+            assert np.array_equal(og, first[0]) and np.array_equal(lg, first[1])
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_kernels_agree(D):
     """Both kernels on one input: each within tolerance of the oracle and of
