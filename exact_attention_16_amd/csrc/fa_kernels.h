@@ -9,8 +9,8 @@
 //    phase and a softmax phase, so each SIMD always holds one multiplying
 //    and one exponentiating wave; K/V in three LDS stages, two tiles ahead.
 //  * fa_fwd_k4 (four waves, 128 query rows), for grids too small to fill the
-//    chip with 256-row tiles: each wave overlaps the next tile's K.Q^T (and,
-//    at D=64, the previous tile's P.V) with its own current softmax.
+//    chip with 256-row tiles: each wave runs a tile start to end, the other
+//    waves on its SIMD covering its latencies.
 //  * fa_fwd_split (fa_split.h), for small grids at D = 64: four groups of
 //    two waves split each query tile's KV tiles, merged in LDS.
 //  * fa_fwd_occ4 (fa_occ4.h), D = 64 without the causal mask on grids that
@@ -62,20 +62,19 @@ fa_fwd_pp_kt(const Problem P) {
 
 
 // ------------------------------------------------------------ four-wave
-// Register pipeline depth per head dimension. D=64: three stages (S(j+1),
-// P(j-1).V(j-1) and softmax(j) in one block) fit two waves per SIMD. D=128:
-// two stages (the history from the tile max alone, the rare rescale, then
-// one block with the exponentials, P(j).V(j) and S(j+1)); the other wave on
-// the SIMD covers the rest.
-template <int D> struct Pipe { static constexpr bool three = D == 64; };
-
+// Each wave runs a tile start to end: S = K Q^T, the softmax (base update
+// from the tile max, the rare rescale of O, exponentials), P.V; K and V in
+// two LDS stages each, the next tile's DMA issued at the top of the step.
+// The other waves on the SIMD cover one wave's latencies. (A register
+// pipeline, the next tile's S and, at D = 64, the previous tile's P.V under
+// the current softmax, took 200-230 registers and ran 5-12% longer on the
+// small grids this kernel serves.)
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_k4(const Problem P) {
   using C = Cfg4<D>;
   using W = Wave<T, C, CAUSAL, THR, DIAG>;
-  constexpr bool P3 = Pipe<D>::three;
   constexpr int NKB = W::NKB, NKC = W::NKC;
   constexpr int TB = C::tileBytes;
   // one array per stage, V stages first in name order (as in fa_fwd_pp)
@@ -92,95 +91,44 @@ fa_fwd_k4(const Problem P) {
   if (!w.init(P)) return;
   const int ntiles = w.group_tiles();
   const int nw = w.wave_tiles();
+  f32x16 s[NKB];
+  u32x4 p[NKC];
 
-  f32x16 sA[NKB], sB[NKB];  // S(j) lives in sA for even j, sB for odd j
-  u32x4 pA[NKC], pB[NKC];   // P(j) likewise (only pA is used with two stages)
-#pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) pB[kc] = (u32x4){};  // P(-1) = 0
-
-  // ---- prologue: K(0), K(1) (and V(0) with two stages) in LDS; S(0) --------
-  // With three stages iteration 0 runs the steady-state block with P(-1) = 0
-  // against V buffer 1, so that buffer must hold finite values (0 * NaN
-  // would poison O).
   w.dma_k(lk0, 0);
-  if (ntiles > 1) w.dma_k(lk1, 1);
-  if constexpr (P3) {
-#pragma unroll
-    for (int i = 0; i < TB / (16 * C::threads); ++i)
-      *(__attribute__((address_space(3))) u32x4*)(lv1 + 16 * (threadIdx.x + i * C::threads)) =
-          (u32x4){};
-  } else {
-    w.dma_v(lv0, 0);
-  }
+  w.dma_v(lv0, 0);
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (nw > 0) w.qk(sA, lk0);
-  __syncthreads();  // b_kstage0 is refilled with K(2) in iteration 0
-
-  // ---- iteration j (PH = j % 2). DMA first (K(j+2); V(j) with three stages,
-  // V(j+1) with two). A wave that still has tile j then computes; at its
-  // last tile the S(j+1) it computes is not used. With three stages
-  // iteration nw only drains P(nw-1).V(nw-1). The wave keeps issuing its
-  // share of the DMA and the barriers until the work-group's last tile.
-  auto iter = [&](auto ph, int j) {
+  wg_barrier();
+  // step j (PH = j % 2): tile j in stage PH; the DMA of tile j+1 into the
+  // other stage (read in step j-1, which every wave has left at the
+  // barrier); a wave past its last visible tile keeps issuing its DMA share
+  // and meeting the barriers
+  auto step = [&](auto ph, int j) {
     constexpr int PH = decltype(ph)::value;
-    f32x16(&scur)[NKB] = pick<PH>(sB, sA);
-    f32x16(&snext)[NKB] = pick<PH>(sA, sB);
-    u32x4(&pcur)[NKC] = P3 ? pick<PH>(pB, pA) : pA;
-    u32x4(&pprev)[NKC] = pick<PH>(pA, pB);
-    lds_char* k_next = PH ? lk0 : lk1;  // holds K(j+1)
-    lds_char* k_dma = PH ? lk1 : lk0;   // receives K(j+2)
-    lds_char* v_cur = PH ? lv1 : lv0;   // V(j) (two stages) / receives V(j) (three)
-    lds_char* v_oth = PH ? lv0 : lv1;   // V(j-1) (three stages) / receives V(j+1) (two)
-    if constexpr (P3) {
-      if (j < ntiles) w.dma_v(v_cur, j);
-    } else {
-      if (j + 1 < ntiles) w.dma_v(v_oth, j + 1);
+    if (j + 1 < ntiles) {
+      w.dma_k(PH ? lk0 : lk1, j + 1);
+      w.dma_v(PH ? lv0 : lv1, j + 1);
     }
-    if (j + 2 < ntiles) w.dma_k(k_dma, j + 2);
     __builtin_amdgcn_sched_barrier(0);
-
     if (j < nw) {
+      w.qk(s, PH ? lk1 : lk0);
+      W::qk_schedule();
       const int kv0 = j * W::BN;
-      if (w.needs_mask(kv0)) w.mask(scur, kv0);
-      if constexpr (P3) {
-        // one block: P(j-1).V(j-1) and S(j+1) MFMAs under softmax(j); the
-        // rescale of O by softmax(j)'s history follows P(j-1).V(j-1). P(j)
-        // and the row sum are pinned in the block instead of sinking past
-        // the rescale branch.
-        w.pv(pprev, v_oth);
-        const float hist = w.softmax_max(scur);
-        w.softmax_exp(scur, pcur);
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(pcur[kc]));
-        asm volatile("" : "+v"(w.lsum));
-        w.qk(snext, k_next);
-        w.rescale(j, hist);
-      } else {
-        // the history is known from the tile max alone: rescale O first,
-        // then one block with the exponentials, P(j).V(j) (each 16-key chunk
-        // as soon as its P is packed) and the S(j+1) MFMAs
-        const float hist = w.softmax_max(scur);
-        w.rescale(j, hist);
-        w.softmax_exp(scur, pcur);
-        w.pv(pcur, v_cur);
-        w.qk(snext, k_next);
-      }
-    } else if (P3 && j == nw) {
-      w.pv(pprev, v_oth);
+      if (w.needs_mask(kv0)) w.mask(s, kv0);
+      const float hist = w.softmax_max(s);
+      w.rescale(j, hist);
+      w.softmax_exp(s, p);
+      w.pv(p, PH ? lv1 : lv0);
+      W::pv_schedule();
     }
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    wg_barrier();
   };
-
-  const int niter = P3 ? ntiles + 1 : ntiles;
   int j = 0;
-  for (; j + 1 < niter; j += 2) {
-    iter(IC<0>{}, j);
-    iter(IC<1>{}, j + 1);
+  for (; j + 1 < ntiles; j += 2) {
+    step(IC<0>{}, j);
+    step(IC<1>{}, j + 1);
   }
-  if (j < niter) iter(IC<0>{}, j);
-
+  if (j < ntiles) step(IC<0>{}, j);
   w.epilogue(P.events);
 }
 
@@ -263,15 +211,16 @@ static int launch_one(Problem P, hipStream_t stream, int variant) {
     }
   } else {
     P.nqt = num_q_tiles(P.Sq, Cfg4<D>::BM);
-    // At D = 128 the kernel's 64 KiB of LDS let two work-groups share a CU.
-    // Run that way, the work-group whose LDS allocation starts above 64 KiB
-    // (the second on the CU) returned wrong rows in some runs (a few rows of
-    // one wave, several work-groups per launch; never a work-group at LDS
-    // base 0, and never when the two work-groups read the same head). 17 KiB
-    // of unused dynamic LDS keep one work-group per CU (81 KiB > 160 / 2);
-    // the cost on the shapes this kernel serves is 0-2% (7% where the grid
-    // then takes two rounds).
-    const unsigned lds_pad = D == 128 ? 17u * 1024u : 0u;
+    // Work-groups whose LDS allocation starts at or above 64 KiB (the second
+    // of two 64 KiB work-groups on a CU) returned wrong rows in some runs (a
+    // few rows of one wave, several work-groups per launch; never one at LDS
+    // base 0, and never when the co-resident work-groups read the same
+    // head). Unused dynamic LDS keeps every allocation below that: at
+    // D = 128 17 KiB (81 KiB, one work-group per CU; 0-2% on the shapes this
+    // kernel serves, 7% where the grid then takes two rounds), at D = 64
+    // 22 KiB (54 KiB, at most two per CU, which its registers would
+    // otherwise allow four of).
+    const unsigned lds_pad = D == 128 ? 17u * 1024u : 22u * 1024u;
     hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
                        dim3(Cfg4<D>::threads), lds_pad, stream, P);
   }

@@ -254,7 +254,12 @@ struct Wave : RowState<C, CAUSAL, THR> {
   // A row's visible keys are a prefix from key 0, so a row whose base is
   // still -inf after its first tile sees no key: all its p are 0 (base 0).
   __device__ __forceinline__ void softmax_tile(f32x16 (&s)[NKB], u32x4 (&p)[NKC], int j) {
-    const int kv0 = j * BN;
+    softmax_tile_at(s, p, j * BN, j);
+  }
+  // The same for the tile at key kv0 that is the j-th tile these rows see
+  // (the key-split kernel's groups take every fourth tile)
+  __device__ __forceinline__ void softmax_tile_at(f32x16 (&s)[NKB], u32x4 (&p)[NKC], int kv0,
+                                                  int j) {
     if (this->needs_mask(kv0)) mask(s, kv0);
     float hist = 1.f;
     if (j == 0) hist = this->softmax_max(s);
