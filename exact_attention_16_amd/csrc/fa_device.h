@@ -183,6 +183,65 @@ __device__ __forceinline__ HeadRows head_rows(const Problem& P, int bb, int h) {
   return r;
 }
 
+// Compacted variable-length launch (varlen_tile in fa_layout.h): the
+// sequence g holding rank k, the rank r within it and its tile count nt.
+// Every wave scans the offsets itself, lane l taking sequences 4l .. 4l+3
+// (at most kCompactMaxSeqs): per-lane item counts, an inclusive sum over the
+// lanes, and the first lane whose sum exceeds k. *dec: some offset is below
+// the one before it (the same for every work-group). False when k is at or
+// past the last item (a work-group of the bound's slack).
+template <int BM>
+__device__ __forceinline__ bool varlen_find(const Problem& P, int m, int k, int* g, int* r,
+                                            int* nt, bool* dec) {
+  const int lane = threadIdx.x & 63;
+  int s[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int idx = 4 * lane + i;
+    s[i] = idx <= P.B ? P.cuq[idx] : 0;
+  }
+  int n[4], tot = 0;
+  bool d = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    n[i] = 0;
+    if (4 * lane + i < P.B) {
+      d |= s[i + 1] < s[i];
+      const int sq = clampi(s[i], 0, P.totq), eq = clampi(s[i + 1], sq, P.totq);
+      n[i] = num_q_tiles(min(eq - sq, P.Sq), BM);
+    }
+    tot += m * n[i];
+  }
+  *dec = __builtin_amdgcn_ballot_w64(d) != 0;
+  int incl = tot;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const int t = __shfl_up(incl, (unsigned)sh, 64);
+    if (lane >= sh) incl += t;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(k < incl);
+  if (hit == 0) return false;
+  const int L = (int)__builtin_ctzll(hit);
+  int rr = k - (incl - tot), gg = 0, nn = 0;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!found) {
+      if (rr < m * n[i]) {
+        gg = 4 * lane + i;
+        nn = n[i];
+        found = true;
+      } else {
+        rr -= m * n[i];
+      }
+    }
+  }
+  *g = __builtin_amdgcn_readlane(gg, L);
+  *r = __builtin_amdgcn_readlane(rr, L);
+  *nt = __builtin_amdgcn_readlane(nn, L);
+  return true;
+}
+
 // What every wave type knows about its rows (configuration C, causal mask,
 // base lag THR in log2 units): which 32 query rows it owns, its sequence's
 // lengths, the running base b of the online softmax and its share of the
@@ -210,7 +269,7 @@ template <class C, bool CAUSAL, int THR> struct RowState {
     asm volatile("" ::"s"(P.qb), "s"(P.qh), "s"(P.qs), "s"(P.kb), "s"(P.kh), "s"(P.ks));
     asm volatile("" ::"s"(P.vb), "s"(P.vh), "s"(P.vs), "s"(P.ob), "s"(P.oh), "s"(P.os));
     asm volatile("" ::"s"(P.lb), "s"(P.lh), "s"(P.cuq), "s"(P.B), "s"(P.H), "s"(P.Sq), "s"(P.Sk));
-    asm volatile("" ::"s"(P.nqt), "s"(P.c), "s"(P.hgroup));
+    asm volatile("" ::"s"(P.nqt), "s"(P.c), "s"(P.hgroup), "s"(P.compact), "s"(P.items), "s"(P.totq));
     const int tid = threadIdx.x;
     lane = tid & 63;
     // (the key-split kernel runs several groups of C::NW waves on the same rows)
@@ -218,7 +277,22 @@ template <class C, bool CAUSAL, int THR> struct RowState {
     hh = lane >> 5;
     c = P.c;
     int bh;
-    block_to_tile(id, P.B * P.H, P.nqt, CAUSAL, &qt, &bh, P.hgroup);
+    if (P.compact) {
+      const bool xcd = (P.H & 7) == 0;
+      const int m = xcd ? P.H >> 3 : P.H;
+      int g, r, nt, j;
+      bool dec;
+      const bool any = varlen_find<C::BM>(P, m, xcd ? id >> 3 : id, &g, &r, &nt, &dec);
+      if (dec) {  // offsets out of order: nothing is computed
+        flag_all_rows(P, id);
+        return false;
+      }
+      if (!any) return false;
+      varlen_tile(r, m, nt, CAUSAL, &qt, &j);
+      bh = g * P.H + (xcd ? (id & 7) + 8 * j : j);
+    } else {
+      block_to_tile(id, P.B * P.H, P.nqt, CAUSAL, &qt, &bh, P.hgroup);
+    }
     const int bb = bh / P.H, h = bh - bb * P.H;
     *hr = head_rows(P, bb, h);
     Lq = hr->Lq;
@@ -254,7 +328,26 @@ template <class C, bool CAUSAL, int THR> struct RowState {
         P.lse[hr.l0 + r] = __builtin_nanf("");
     };
     mark(qt * C::BM, min(hr.Lq, (qt + 1) * C::BM));
-    if (qt == P.nqt - 1) mark(hr.Lq, hr.Lq + hr.cut_q);
+    if (qt == num_q_tiles(hr.Lq, C::BM) - 1) mark(hr.Lq, hr.Lq + hr.cut_q);
+  }
+  // Variable lengths (compacted launch) with offsets that decrease somewhere,
+  // against the stated order: the launch's bound no longer covers every
+  // tile, so no sequence is computed and every token row of every head gets
+  // NaN in O and lse. Work item id of the P.items marks token rows
+  // [t0, t1), its share of the totq, in every head.
+  __device__ void flag_all_rows(const Problem& P, int id) const {
+    const unsigned G = (unsigned)P.items, n = (unsigned)P.totq;
+    const unsigned per = n / G, rem = n % G, u = (unsigned)id;
+    const int t0 = (int)(u * per + (u < rem ? u : rem));
+    const int t1 = t0 + (int)per + (u < rem);
+    unsigned short* const o = (unsigned short*)P.o;
+    const int cnt = (t1 - t0) * C::D;
+    for (int h = 0; h < P.H; ++h) {
+      for (int i = threadIdx.x; i < cnt; i += blockDim.x)
+        o[(long long)(t0 + i / C::D) * P.os + h * P.oh + i % C::D] = 0xFFFFu;
+      for (int t = t0 + (int)threadIdx.x; t < t1; t += (int)blockDim.x)
+        P.lse[h * P.lh + t] = __builtin_nanf("");
+    }
   }
 
   __device__ __forceinline__ void reset_softmax() {

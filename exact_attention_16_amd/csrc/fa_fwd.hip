@@ -64,7 +64,8 @@ namespace fa {
 template <typename T> static int launch_kt(Problem P, int D, int causal, hipStream_t st) {
   static_assert(CfgKT<64>::BM == CfgKT<128>::BM, "one query tile size for both head dims");
   P.nqt = num_q_tiles(P.Sq, CfgKT<128>::BM);
-  const dim3 grid((unsigned)P.nqt * (unsigned)(P.B * P.H)), block(512);
+  P.items = P.nqt * P.B * P.H;
+  const dim3 grid((unsigned)P.items), block(512);
   if (D == 64) {
     if (causal) hipLaunchKernelGGL((fa_fwd_pp_kt<T, 64, true>), grid, block, 0, st, P);
     else hipLaunchKernelGGL((fa_fwd_pp_kt<T, 64, false>), grid, block, 0, st, P);

@@ -275,7 +275,8 @@ fa_fwd_il8(const Problem P) {
 // longer.)
 template <int D> static int launch_fp8_d(Problem P, int causal, hipStream_t stream) {
   P.nqt = num_q_tiles(P.Sq, CfgF8il<D>::BM);
-  const dim3 grid((unsigned)P.nqt * (unsigned)(P.B * P.H)), block(CfgF8il<D>::threads);
+  P.items = P.nqt * P.B * P.H;
+  const dim3 grid((unsigned)P.items), block(CfgF8il<D>::threads);
   if (causal)
     hipLaunchKernelGGL((fa_fwd_il8<D, true>), grid, block, 0, stream, P);
   else

@@ -178,13 +178,31 @@ static inline int persistent_groups() {
   return cus / 8 * 8;
 }
 
+// The work items of a launch with query tiles of BM rows (P.nqt, P.items,
+// P.compact): every (Q tile, sequence, head), or for a variable-length batch
+// of at most kCompactMaxSeqs sequences only the tiles within the sequences,
+// up to the bound varlen_cap (fa_layout.h) when that is smaller.
+template <int BM> static inline void set_items(Problem& P) {
+  P.nqt = num_q_tiles(P.Sq, BM);
+  const long long full = (long long)P.nqt * P.B * P.H;  // below 2^31 (validated)
+  P.items = (int)full;
+  P.compact = 0;
+  if (P.cuq && P.B <= kCompactMaxSeqs) {
+    const long long cap = varlen_cap(P.totq, P.B, P.nqt, BM) * P.H;
+    if (cap < full) {
+      P.items = (int)cap;
+      P.compact = 1;
+    }
+  }
+}
+
 // One launch of the kernel `variant` selects for a filled, validated Problem.
 template <typename T, int D, bool CAUSAL, int THR, bool DIAG>
 static int launch_one(Problem P, hipStream_t stream, int variant) {
   const int BH = P.B * P.H;
   if (DIAG && variant == kPersistent) {
     if constexpr (DIAG) {
-      P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);
+      set_items<Cfg8<D>::BM>(P);
       const int g = persistent_groups();
       if (g <= 0) return FA_ERR_HIP;
       hipLaunchKernelGGL((fa_fwd_pp_persist<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)g),
@@ -193,24 +211,23 @@ static int launch_one(Problem P, hipStream_t stream, int variant) {
   } else if (use_occ4<D, CAUSAL>(BH, P.Sq, variant)) {
     // the product library runs it without the causal mask only
     if constexpr (D == 64 && (!CAUSAL || DIAG)) {
-      P.nqt = num_q_tiles(P.Sq, CfgOcc4<D>::BM);
+      set_items<CfgOcc4<D>::BM>(P);
       hipLaunchKernelGGL((fa_fwd_occ4<T, D, CAUSAL, THR, DIAG>),
-                         dim3((unsigned)P.nqt * (unsigned)BH), dim3(CfgOcc4<D>::threads), 0,
+                         dim3((unsigned)P.items), dim3(CfgOcc4<D>::threads), 0,
                          stream, P);
     }
   } else if (use_pingpong<D>(BH, P.Sq, variant)) {
-    P.nqt = num_q_tiles(P.Sq, Cfg8<D>::BM);
-    hipLaunchKernelGGL((fa_fwd_pp<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+    set_items<Cfg8<D>::BM>(P);
+    hipLaunchKernelGGL((fa_fwd_pp<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.items),
                        dim3(Cfg8<D>::threads), 0, stream, P);
   } else if (use_split<D>(BH, P.Sq, variant)) {
     if constexpr (D == 64) {
-      P.nqt = num_q_tiles(P.Sq, CfgSplit<D>::BM);
-      hipLaunchKernelGGL((fa_fwd_split<T, D, CAUSAL, THR, DIAG>),
-                         dim3((unsigned)P.nqt * (unsigned)BH),
+      set_items<CfgSplit<D>::BM>(P);
+      hipLaunchKernelGGL((fa_fwd_split<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.items),
                          dim3(CfgSplit<D>::threads * kSplitGroups), 0, stream, P);
     }
   } else {
-    P.nqt = num_q_tiles(P.Sq, Cfg4<D>::BM);
+    set_items<Cfg4<D>::BM>(P);
     // Work-groups whose LDS allocation starts at or above 64 KiB (the second
     // of two 64 KiB work-groups on a CU) returned wrong rows in some runs (a
     // few rows of one wave, several work-groups per launch; never one at LDS
@@ -221,7 +238,7 @@ static int launch_one(Problem P, hipStream_t stream, int variant) {
     // 22 KiB (54 KiB, at most two per CU, which its registers would
     // otherwise allow four of).
     const unsigned lds_pad = D == 128 ? 17u * 1024u : 22u * 1024u;
-    hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.nqt * (unsigned)BH),
+    hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.items),
                        dim3(Cfg4<D>::threads), lds_pad, stream, P);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;

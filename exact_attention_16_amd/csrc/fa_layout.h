@@ -108,6 +108,40 @@ FA_HD void block_to_tile(int bid, int BH, int nqt, bool causal, int* qt, int* bh
 // for S near INT_MAX)
 FA_HD int num_q_tiles(int S, int BM) { return S / BM + (S % BM != 0); }
 
+// Variable lengths: a launch sized for the longest sequence gives every
+// shorter one query tiles that lie wholly past its end (work-groups that only
+// start and return). For batches of at most kCompactMaxSeqs sequences the
+// launch runs only the tiles within each sequence. The lengths are on the
+// device, so the launch takes the bound below and each work-group finds its
+// item from the offsets (RowState::locate). With offsets that never
+// decrease, sequence b has L_b <= its token count query rows, the counts sum
+// to at most totq, and the sum of ceil(L_b / BM) is at most
+// floor((totq + B*(BM-1)) / BM); never more than the B * nqt of the full grid.
+constexpr int kCompactMaxSeqs = 256;  // one pass of a 64-lane scan, 4 per lane
+FA_HD long long varlen_cap(int totq, int B, int nqt, int BM) {
+  const long long full = (long long)B * nqt;
+  const long long cap = ((long long)totq + (long long)B * (BM - 1)) / BM;
+  return cap < full ? cap : full;
+}
+// Item order of a compacted launch. With H a multiple of 8, work-group id
+// runs on XCD x = id mod 8 and takes rank k = id / 8 there, over the m = H/8
+// heads x, x+8, ... of each sequence (the heads one sequence puts on an XCD);
+// otherwise x = 0, k = id, over all m = H heads. Ranks run over the
+// sequences in order, m * nt_b ranks for sequence b with nt_b query tiles.
+// Within a sequence (rank r): causal, heaviest tile first with the m heads
+// in turn; else one head at a time. Returns the tile and the head index j
+// among the m (head x + 8j, or j).
+FA_HD void varlen_tile(int r, int m, int nt, bool causal, int* qt, int* j) {
+  if (causal) {
+    const int ord = r / m;
+    *j = r - ord * m;
+    *qt = nt - 1 - ord;
+  } else {
+    *j = r / nt;
+    *qt = r - *j * nt;
+  }
+}
+
 // Work item of a persistent work-group b (of G, a multiple of 8) at round k:
 // a snake over the ranks of its XCD (see pp_persistent); -1 past the last.
 FA_HD int persistent_item(int b, int G, int k, int total) {

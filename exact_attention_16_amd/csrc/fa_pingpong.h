@@ -56,7 +56,8 @@ template <class W> __device__ __forceinline__ void pp_body(const Problem& P) {
 // a new launch per item. Work-group b on XCD x = b mod 8 (index c = b / 8
 // among the G/8 work-groups of its XCD) takes, at round k, the item of rank
 // k*G/8 + c on its XCD for even k and k*G/8 + G/8 - 1 - c for odd k: ranks
-// follow the launch order of block_to_tile (heaviest first when causal), so
+// follow the launch order (block_to_tile, or varlen_tile for a compacted
+// variable-length launch; heaviest first when causal), so
 // the snake pairs heavy items with light ones. Its item ids rise with k,
 // so the first id past the end ends the work-group.
 template <class W> __device__ __forceinline__ void pp_persistent(const Problem& P) {
@@ -64,7 +65,7 @@ template <class W> __device__ __forceinline__ void pp_persistent(const Problem& 
   constexpr int TB = C::tileBytes;
   FA_PP_STAGES(TB)
 
-  const int total = P.nqt * P.B * P.H;
+  const int total = P.items;
   for (int k = 0;; ++k) {
     const int id = persistent_item(blockIdx.x, gridDim.x, k, total);
     if (id < 0) break;

@@ -33,6 +33,10 @@ struct Problem {
   unsigned long long* events;  // rescale-event counter of the diagnostic kernels
   float vscale;  // 8-bit inputs: the V descale, applied to O at the end
   int hgroup;    // causal: heads an XCD takes together (block_to_tile)
+  int items;     // work items (Q tile, sequence, head) the launch runs
+  int compact;   // variable lengths: items are only the query tiles within
+                 // each sequence (varlen_tile in fa_layout.h), else all
+                 // nqt * B * H of them
 };
 
 }  // namespace fa

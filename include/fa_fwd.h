@@ -143,10 +143,22 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
  *            non-decreasing: sequence b has query tokens cu_seqlens_q[b] ..
  *            cu_seqlens_q[b+1]-1 and key tokens cu_seqlens_k[b] ..
  *            cu_seqlens_k[b+1]-1. Read by the kernel; owned by the caller.
- *   max_seqlen_q, max_seqlen_k   upper bounds of the lengths (they size the
- *            grid). A sequence longer than max_seqlen_q, or with more keys
- *            than max_seqlen_k, is not computed: all its rows get NaN in o
- *            and lse (the other sequences are unaffected).
+ *            Offsets out of order are not an error the call can return: no
+ *            memory outside the tensors is touched either way, and with at
+ *            most 256 sequences, cu_seqlens_q out of order computes nothing
+ *            and sets every row of o and lse to NaN.
+ *   max_seqlen_q, max_seqlen_k   upper bounds of the lengths. A sequence
+ *            longer than max_seqlen_q, or with more keys than max_seqlen_k,
+ *            is not computed: all its rows get NaN in o and lse (the other
+ *            sequences are unaffected).
+ *   Work-groups: one per query tile of each (sequence, head). With at most
+ *            256 sequences the launch holds H * min(B * ceil(max_seqlen_q /
+ *            BM), floor((total_q + B * (BM - 1)) / BM)) work-groups (BM the
+ *            kernel's query rows per tile; the second term bounds the tiles
+ *            the sequences can have, since their lengths are on the device),
+ *            and each finds its (sequence, tile, head) from the offsets, so
+ *            no work-group is spent on tiles past a sequence's end; with more
+ *            sequences, H * B * ceil(max_seqlen_q / BM).
  *   total_q, total_k   token rows q/o/lse and k/v hold; the kernel clamps
  *            every offset to them, so a bad offset array cannot address
  *            memory outside the tensors.

@@ -17,6 +17,8 @@
 //    past the end (so the buffer range check drops or zero-fills them whole);
 //  * the work decomposition visits each (Q tile, head) once, every key a row
 //    can see lies in a tile its wave computes, and O is written exactly once;
+//    a compacted variable-length launch visits each query tile within the
+//    sequences once;
 //  * the worst LDS bank-conflict degree of every pattern, under a 64-bank
 //    model (256 bytes per cycle) and a 32-bank model (128 bytes per cycle);
 //  * the eight-wave ping-pong schedule: replaying both wave groups' slots
@@ -547,6 +549,119 @@ static void check_tile_map() {
         }
 }
 
+// The compacted variable-length launch (varlen_cap, varlen_tile): for
+// offset arrays that never decrease, the bound covers every query tile within
+// the sequences, and ids below it map one-to-one onto those tiles (the rest
+// onto nothing), each head on XCD head mod 8 when H is a multiple of 8, a
+// sequence's causal tiles heaviest first. The sequence search is done twice:
+// a plain walk over the sequences, and the kernel's lane-parallel form
+// (varlen_find: four sequences per lane, an inclusive sum over 64 lanes, the
+// first lane whose sum exceeds the rank, a walk of that lane's four).
+static bool find_plain(const std::vector<int>& cnt, int k, int* g, int* r) {
+  for (int b = 0; b < (int)cnt.size(); ++b) {
+    if (k < cnt[b]) {
+      *g = b;
+      *r = k;
+      return true;
+    }
+    k -= cnt[b];
+  }
+  return false;
+}
+static bool find_lanes(const std::vector<int>& cnt, int k, int* g, int* r) {
+  const int B = (int)cnt.size();
+  int tot[64], incl[64];
+  for (int l = 0; l < 64; ++l) {
+    tot[l] = 0;
+    for (int i = 0; i < 4; ++i)
+      if (4 * l + i < B) tot[l] += cnt[4 * l + i];
+  }
+  for (int l = 0; l < 64; ++l) incl[l] = tot[l] + (l ? incl[l - 1] : 0);
+  int L = -1;
+  for (int l = 0; l < 64 && L < 0; ++l)
+    if (k < incl[l]) L = l;
+  if (L < 0) return false;
+  int rr = k - (incl[L] - tot[L]);
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * L + i < B ? cnt[4 * L + i] : 0;
+    if (rr < c) {
+      *g = 4 * L + i;
+      *r = rr;
+      return true;
+    }
+    rr -= c;
+  }
+  return false;
+}
+static void check_varlen_map() {
+  unsigned seed = 12345u;
+  auto rnd = [&](int n) {
+    seed = seed * 1103515245u + 12345u;
+    return (int)((seed >> 8) % (unsigned)n);
+  };
+  const int Hs[] = {1, 3, 8, 16, 24};
+  const int Bs[] = {1, 2, 7, 63, 64, 65, 200, kCompactMaxSeqs};
+  const int BMs[] = {64, 128, 256};
+  long checked = 0;
+  for (int H : Hs)
+    for (int B : Bs)
+      for (int BM : BMs)
+        for (int causal = 0; causal < 2; ++causal)
+          for (int rep = 0; rep < 3; ++rep) {
+            // lengths: a mix of empty, short and long sequences; Sq is the
+            // longest (rep 2: some sequences past a stated maximum)
+            std::vector<int> len(B);
+            int Sq = 1, totq = 0;
+            for (int b = 0; b < B; ++b) {
+              const int kind = rnd(4);
+              len[b] = kind == 0 ? 0 : kind == 1 ? 1 + rnd(BM) : 1 + rnd(20 * BM);
+              totq += len[b];
+              Sq = std::max(Sq, len[b]);
+            }
+            if (rep == 2) Sq = std::max(1, Sq / 2);
+            const int nqt = num_q_tiles(Sq, BM);
+            const bool xcd = H % 8 == 0;
+            const int m = xcd ? H / 8 : H;
+            std::vector<int> nt(B), cnt(B);
+            long need = 0;
+            for (int b = 0; b < B; ++b) {
+              nt[b] = num_q_tiles(std::min(len[b], Sq), BM);
+              cnt[b] = m * nt[b];
+              need += nt[b];
+            }
+            const long long cap = varlen_cap(totq, B, nqt, BM);
+            CHECK(need <= cap, "varlen bound %lld below the %ld tiles", cap, need);
+            const long long items = cap * H;
+            std::map<long long, int> seen;  // (b, h, qt) -> id
+            std::vector<int> last_qt((size_t)B * H, 1 << 30);
+            for (long long id = 0; id < items; ++id) {
+              const int k = xcd ? (int)(id >> 3) : (int)id;
+              int g, r, g2, r2;
+              const bool any = find_plain(cnt, k, &g, &r);
+              const bool any2 = find_lanes(cnt, k, &g2, &r2);
+              CHECK(any == any2 && (!any || (g == g2 && r == r2)), "lane search differs");
+              if (!any) continue;
+              int qt, j;
+              varlen_tile(r, m, nt[g], causal != 0, &qt, &j);
+              const int h = xcd ? (int)(id & 7) + 8 * j : j;
+              CHECK(qt >= 0 && qt < nt[g] && h >= 0 && h < H, "varlen tile out of range");
+              if (!(qt >= 0 && qt < nt[g] && h >= 0 && h < H)) continue;
+              const long long key = ((long long)g * H + h) * nqt + qt;
+              CHECK(!seen.count(key), "varlen tile twice B=%d H=%d BM=%d", B, H, BM);
+              seen[key] = (int)id;
+              if (xcd) CHECK(h % 8 == id % 8, "varlen head off its XCD");
+              if (causal) {
+                CHECK(qt < last_qt[(size_t)g * H + h], "varlen causal tiles out of order");
+                last_qt[(size_t)g * H + h] = qt;
+              }
+              ++checked;
+            }
+            CHECK((long)seen.size() == need * H, "varlen tiles missed: %zu of %ld", seen.size(),
+                  need * H);
+          }
+  std::printf("varlen compacted map: %ld work items checked\n", checked);
+}
+
 // ------------------------------------------------ ping-pong schedule replay
 // One DMA share (one wave's issues) of a tile into a stage.
 struct Share {
@@ -747,6 +862,7 @@ int main() {
   check_lds<CfgSplitG>();
   check_lds<CfgOcc>();
   check_tile_map();
+  check_varlen_map();
   std::printf("work-group map: every head-group size: checked\n");
   // persistent work-groups: every item exactly once, ids rising per group
   for (int G : {8, 16, 256, 264})

@@ -298,3 +298,96 @@ def test_varlen_offsets_past_the_tensors_are_clamped():
                                            float(np.float32(1.0 / math.sqrt(D))))
     _assert_close(o_to_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, dtype,
                   "varlen clamped")
+
+
+# A variable-length launch of at most 256 sequences runs only the query tiles
+# within the sequences (each work-group finds its tile from the offsets); a
+# larger batch runs the full grid. The outputs start as NaN, so a row that no
+# work-group writes fails the comparison.
+
+def _run_varlen_prefilled(cq, ck, qb, kb, vb, dtype, causal, max_q, max_k):
+    dev = device()
+    H, D = qb.shape[1], qb.shape[2]
+    out = torch.full(qb.shape, float("nan"), dtype=TORCH_DT[dtype], device=dev)
+    lse = torch.full((H, qb.shape[0]), float("nan"), dtype=torch.float32, device=dev)
+    cu_q = torch.from_numpy(cq).to(dev)
+    cu_k = torch.from_numpy(ck).to(dev)
+    fa.attention_varlen(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), cu_q, cu_k,
+                        max_q, max_k, causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o_to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _skewed_lengths(rng, B, short, long_lens):
+    """B sequences: short ones (0 .. short-1 tokens, some empty) with the long
+    ones placed among them."""
+    L = [int(x) for x in rng.integers(0, short, size=B - len(long_lens))]
+    for n, x in enumerate(long_lens):
+        L.insert((n + 1) * len(L) // (len(long_lens) + 1), x)
+    return L
+
+
+@pytest.mark.parametrize("H", [3, 8])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_compacted_launch_all_rows(causal, D, H):
+    """One long sequence among 40 short or empty ones: the full grid would be
+    mostly query tiles past the sequences' ends. H = 8 takes the XCD order
+    (heads x, x+8, ... of each sequence per XCD), H = 3 the plain one."""
+    dtype = W.BF16
+    rng = np.random.default_rng(200 + D + H + causal)
+    lq = _skewed_lengths(rng, 41, 120, [2048])
+    lk = list(lq)
+    tag = f"varlen compacted causal={causal} D={D} H={H}"
+    _banner(tag)
+    cq, ck, qb, kb, vb = _varlen_inputs(lq, lk, H, D, dtype, 210 + D + H)
+    og, lg = _run_varlen_prefilled(cq, ck, qb, kb, vb, dtype, causal, max(lq), max(lk))
+    o_ref, l_ref = oracle.attention_varlen(W.decode(qb, dtype), W.decode(kb, dtype),
+                                           W.decode(vb, dtype), cq, ck, causal,
+                                           float(np.float32(1.0 / math.sqrt(D))))
+    _assert_close(og, lg, o_ref, l_ref, dtype, tag)
+
+
+@pytest.mark.parametrize("B,H,causal", [(200, 8, True), (256, 2, False), (300, 2, True)])
+def test_varlen_many_sequences_all_rows(B, H, causal):
+    """200 and 256 sequences span many lanes of the work-groups' offset scan
+    (four sequences per lane); 300 is past the compacted launch's limit and
+    runs the full grid."""
+    dtype, D = W.F16, 64
+    rng = np.random.default_rng(230 + B)
+    lq = _skewed_lengths(rng, B, 90, [700, 1300])
+    lk = [max(0, x + int(d)) for x, d in zip(lq, rng.integers(-20, 21, size=B))]
+    tag = f"varlen B={B} H={H} causal={causal}"
+    _banner(tag)
+    cq, ck, qb, kb, vb = _varlen_inputs(lq, lk, H, D, dtype, 240 + B)
+    og, lg = _run_varlen_prefilled(cq, ck, qb, kb, vb, dtype, causal, max(lq), max(lk))
+    o_ref, l_ref = oracle.attention_varlen(W.decode(qb, dtype), W.decode(kb, dtype),
+                                           W.decode(vb, dtype), cq, ck, causal,
+                                           float(np.float32(1.0 / math.sqrt(D))))
+    _assert_close(og, lg, o_ref, l_ref, dtype, tag)
+
+
+@pytest.mark.parametrize("H", [2, 64])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_decreasing_offsets_mark_every_row(causal, D, H):
+    """Offsets that decrease, against the stated order, in a compacted launch:
+    no sequence is computed and every row of O and lse is NaN. (H = 2 runs
+    the four-wave kernel at D = 128 and the key-split kernel at D = 64, H = 64
+    the 256-row kernels.)"""
+    dtype = W.BF16
+    _banner(f"varlen decreasing offsets causal={causal} D={D} H={H}")
+    cq = np.array([0, 100, 50, 200, 400], dtype=np.int32)
+    ck = np.array([0, 100, 150, 200, 400], dtype=np.int32)
+    qb = _bits((400, H, D), dtype, 260)
+    kb = _bits((400, H, D), dtype, 261)
+    vb = _bits((400, H, D), dtype, 262)
+    og, lg = _run_varlen_prefilled(cq, ck, qb, kb, vb, dtype, causal, 2000, 2000)
+    assert np.all(np.isnan(og)) and np.all(np.isnan(lg))
+    # the same offsets in order compute every row
+    cq_ok = np.array([0, 50, 100, 200, 400], dtype=np.int32)
+    og, lg = _run_varlen_prefilled(cq_ok, ck, qb, kb, vb, dtype, causal, 2000, 2000)
+    o_ref, l_ref = oracle.attention_varlen(W.decode(qb, dtype), W.decode(kb, dtype),
+                                           W.decode(vb, dtype), cq_ok, ck, causal,
+                                           float(np.float32(1.0 / math.sqrt(D))))
+    _assert_close(og, lg, o_ref, l_ref, dtype, f"varlen ordered offsets causal={causal} D={D} H={H}")
