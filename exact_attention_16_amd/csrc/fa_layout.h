@@ -50,10 +50,10 @@ template <int D_, int NW_, int BN_, int RPW_ = kRowsPerWave, int ES_ = 2> struct
   static_assert(RPW % kRowsPerWave == 0, "a wave owns whole 32-row blocks");
 };
 
-// The kernels: four waves (128 query rows) with a two- or three-stage
-// register pipeline per wave, for grids too small to fill the chip with
-// 256-row tiles; eight waves (256 rows) in two groups that alternate MFMA
-// and softmax phases (ping-pong). The ping-pong kernel uses 128-key tiles at
+// Two of the kernels' shapes: four waves (128 query rows), each running a
+// tile start to end, for grids too small to fill the chip with 256-row
+// tiles; eight waves (256 rows) in two groups that alternate MFMA and
+// softmax phases (ping-pong). The ping-pong kernel uses 128-key tiles at
 // D=64 so that an MFMA phase (32 MFMAs) balances a softmax phase.
 template <int D> using Cfg4 = Cfg<D, 4, 64>;
 template <int D> using Cfg8 = Cfg<D, 8, (D == 64 ? 128 : 96)>;
