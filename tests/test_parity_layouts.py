@@ -391,3 +391,24 @@ def test_varlen_decreasing_offsets_mark_every_row(causal, D, H):
                                            W.decode(vb, dtype), cq_ok, ck, causal,
                                            float(np.float32(1.0 / math.sqrt(D))))
     _assert_close(og, lg, o_ref, l_ref, dtype, f"varlen ordered offsets causal={causal} D={D} H={H}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_partial_final_tiles_all_rows(causal):
+    """Sixteen sequences whose last 256-row query tile holds 1-128 rows: in
+    those tiles the second group of four waves has no rows and only takes its
+    share of the K/V loads and barriers. Every row of the ping-pong kernel's
+    result against the oracle, outputs filled with NaN first."""
+    dtype, D, H = W.BF16, 128, 8
+    rng = np.random.default_rng(270 + causal)
+    lq = [256 * int(m) + int(r) for m, r in zip(rng.integers(0, 4, size=16), rng.integers(1, 129, size=16))]
+    lk = list(lq)
+    assert fa.fa_fwd_tile(D, len(lq), H, max(lq))[2] == 512
+    tag = f"varlen partial final tiles causal={causal}"
+    _banner(tag)
+    cq, ck, qb, kb, vb = _varlen_inputs(lq, lk, H, D, dtype, 280 + causal)
+    og, lg = _run_varlen_prefilled(cq, ck, qb, kb, vb, dtype, causal, max(lq), max(lk))
+    o_ref, l_ref = oracle.attention_varlen(W.decode(qb, dtype), W.decode(kb, dtype),
+                                           W.decode(vb, dtype), cq, ck, causal,
+                                           float(np.float32(1.0 / math.sqrt(D))))
+    _assert_close(og, lg, o_ref, l_ref, dtype, tag)
