@@ -240,21 +240,36 @@ struct Wave8 : RowState<C_, CAUSAL, THR> {
     const auto ro = FA_RSRC(Oh, (uint32_t)Lq * rso);
     const auto rl = FA_RSRC(Lh, (uint32_t)Lq * 4u);
     const float inv = ltot > 0.f ? vscale / ltot : 0.f;
+    // As in the 16-bit wave's store_rows: everything packed first, and no
+    // store's data registers written after it.
+    static_assert(NDB == 2 || NDB == 4, "head dimension 64 or 128");
+    u32x2 w[NDB][4];
 #pragma unroll
     for (int jd = 0; jd < NDB; ++jd)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x16& a = o[jd];
-        const u32x2 w = {pack2_bf16(a[4 * u + 0] * inv, a[4 * u + 1] * inv),
-                         pack2_bf16(a[4 * u + 2] * inv, a[4 * u + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b64(w, ro, o8_frag_off(qrow, jd, u, hh, rso), 0, 0);
+        w[jd][u] = (u32x2){pack2_bf16(a[4 * u + 0] * inv, a[4 * u + 1] * inv),
+                           pack2_bf16(a[4 * u + 2] * inv, a[4 * u + 3] * inv)};
       }
-    if (hh == 0) {
-      const float l2 =
-          ltot > 0.f ? (b - (float)PSH + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l2), rl,
-                                            (uint32_t)qrow * 4u, 0, 0);
-    }
+    const float l2 =
+        ltot > 0.f ? (b - (float)PSH + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+    const uint32_t lbits = __builtin_bit_cast(uint32_t, l2);
+    if (hh == 0) __builtin_amdgcn_raw_buffer_store_b32(lbits, rl, (uint32_t)qrow * 4u, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jd = 0; jd < NDB; ++jd)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_raw_buffer_store_b64(w[jd][u], ro, o8_frag_off(qrow, jd, u, hh, rso), 0, 0);
+    if constexpr (NDB == 4)
+      asm volatile("" ::"v"(w[0][0]), "v"(w[0][1]), "v"(w[0][2]), "v"(w[0][3]), "v"(w[1][0]),
+                   "v"(w[1][1]), "v"(w[1][2]), "v"(w[1][3]), "v"(w[2][0]), "v"(w[2][1]),
+                   "v"(w[2][2]), "v"(w[2][3]), "v"(w[3][0]), "v"(w[3][1]), "v"(w[3][2]),
+                   "v"(w[3][3]), "v"(lbits));
+    else
+      asm volatile("" ::"v"(w[0][0]), "v"(w[0][1]), "v"(w[0][2]), "v"(w[0][3]), "v"(w[1][0]),
+                   "v"(w[1][1]), "v"(w[1][2]), "v"(w[1][3]), "v"(lbits));
   }
 };
 

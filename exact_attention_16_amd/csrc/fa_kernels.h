@@ -228,15 +228,13 @@ static int launch_one(Problem P, hipStream_t stream, int variant) {
     }
   } else {
     set_items<Cfg4<D>::BM>(P);
-    // Work-groups whose LDS allocation starts at or above 64 KiB (the second
-    // of two 64 KiB work-groups on a CU) returned wrong rows in some runs (a
-    // few rows of one wave, several work-groups per launch; never one at LDS
-    // base 0, and never when the co-resident work-groups read the same
-    // head). Unused dynamic LDS keeps every allocation below that: at
-    // D = 128 17 KiB (81 KiB, one work-group per CU; 0-2% on the shapes this
-    // kernel serves, 7% where the grid then takes two rounds), at D = 64
-    // 22 KiB (54 KiB, at most two per CU, which its registers would
-    // otherwise allow four of).
+    // Unused dynamic LDS sets how many work-groups share a CU: at D = 128
+    // 17 KiB (81 KiB, one per CU), at D = 64 22 KiB (54 KiB, at most two).
+    // Timed against no padding (two per CU at D = 128): B=1 H=48 S=1024
+    // causal 29.4 against 32.5 us, H=63 32.8 against 31.3, the other shapes
+    // this kernel serves within 1%. (Two per CU once returned wrong rows; the
+    // cause was the store-data reuse that store_rows in fa_wave.h now avoids,
+    // and with that fix neither form returns a wrong row.)
     const unsigned lds_pad = D == 128 ? 17u * 1024u : 22u * 1024u;
     hipLaunchKernelGGL((fa_fwd_k4<T, D, CAUSAL, THR, DIAG>), dim3((unsigned)P.items),
                        dim3(Cfg4<D>::threads), lds_pad, stream, P);

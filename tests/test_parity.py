@@ -112,10 +112,12 @@ def test_many_tiles_all_rows(causal, D, kernel):
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
 def test_four_wave_d128_many_work_groups_all_rows(dtype):
-    """B=1 H=63 S=1024 D=128 causal: 504 four-wave work-groups, more than one
-    per CU if two could share one. Run two to a CU, the second work-group on a
-    CU returned wrong rows in some launches (a few rows per launch); the
-    launch keeps one per CU. All rows of every head, three launches."""
+    """B=1 H=63 S=1024 D=128 causal: 504 four-wave work-groups, one per CU,
+    their DMA traffic overlapping other work-groups' epilogues. Before the
+    epilogue packed every value ahead of its stores, a 16-byte O store read
+    its data registers after the next instruction had overwritten them in a
+    few rows of every launch of this grid (run two work-groups to a CU). All
+    rows of every head, three launches, bitwise equal."""
     B, H, S, D = 1, 63, 1024, 128
     assert _auto_kernel(D, B, H, S, True) == "k4"
     qb, kb, vb = (W.random_bits((B, H, S, D), dtype, 7100 + i) for i in range(3))
