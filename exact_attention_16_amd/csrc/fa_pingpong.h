@@ -138,7 +138,11 @@ __device__ __forceinline__ void pp_item(const Problem& P, W& w, lds_char* const 
     // the softmax phase of S(j). K(j) sits in stage R, V(j-1) in stage R-1.
     // The MFMA phase runs at raised wave priority, so that on each SIMD the
     // multiplying wave's MFMAs and LDS reads issue ahead of the other
-    // wave's exponentials whenever both are ready.
+    // wave's exponentials whenever both are ready. Group B's softmax phase
+    // and DMA issue keep that priority too: its step (MFMA phase, softmax,
+    // DMA issue) is the longer chain, which group A waits for at the barrier
+    // (ramp 455 against 467 us, long 445 against 446, the other shapes within
+    // noise).
     auto step = [&](auto r, int j) {
       constexpr int R = decltype(r)::value;
       __builtin_amdgcn_s_setprio(1);
@@ -158,7 +162,7 @@ __device__ __forceinline__ void pp_item(const Problem& P, W& w, lds_char* const 
       } else {
         end_slot();
       }
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(G == 1 ? 1 : 0);
       __builtin_amdgcn_sched_barrier(0);
       if (j < nw) w.softmax_tile(s, p, j);
       // group B's DMA share goes after its softmax work, clear of group A's
