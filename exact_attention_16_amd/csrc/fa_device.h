@@ -341,10 +341,10 @@ template <class C, bool CAUSAL, int THR> struct RowState {
     const int t0 = (int)(u * per + (u < rem ? u : rem));
     const int t1 = t0 + (int)per + (u < rem);
     unsigned short* const o = (unsigned short*)P.o;
-    const int cnt = (t1 - t0) * C::D;
+    const long long cnt = (long long)(t1 - t0) * C::D;  // a few work-groups may hold many rows
     for (int h = 0; h < P.H; ++h) {
-      for (int i = threadIdx.x; i < cnt; i += blockDim.x)
-        o[(long long)(t0 + i / C::D) * P.os + h * P.oh + i % C::D] = 0xFFFFu;
+      for (long long i = threadIdx.x; i < cnt; i += blockDim.x)
+        o[(t0 + i / C::D) * P.os + h * P.oh + (int)(i % C::D)] = 0xFFFFu;
       for (int t = t0 + (int)threadIdx.x; t < t1; t += (int)blockDim.x)
         P.lse[h * P.lh + t] = __builtin_nanf("");
     }
